@@ -1,0 +1,179 @@
+/*
+ * tp_mlp_shard.h -- C ABI of the tensor-parallel MLP shard library (libtpmlp.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  One rank of a Megatron-style tensor-parallel MLP block holds a
+ * column block A_i of the first weight and the matching row block B_i of the
+ * second weight, and computes the full-shape partial
+ *
+ *     P_i = act(X A_i) B_i                       (one tp_mlp_shard_fwd call)
+ *
+ * The layer output is the sum of the partials of all ranks,
+ *
+ *     Z = sum_i P_i                              (one tp_partials_reduce call)
+ *
+ * which tensor parallelism obtains with an all-reduce; here the k partials are
+ * held on one GPU and summed on it.  Sources:
+ *   - page "大模型推理系统揭秘（07）Multi-GPU", section 1.2.2 (column- and
+ *     row-parallel split of Y = XW), section 1.2.3 (the column output shard is the
+ *     row input shard; Z = Z_0 + ... + Z_3), section 1.2.4 (gate/up projections
+ *     column-parallel, activation local to the GPU, down projection row-parallel,
+ *     one all-reduce after the MLP);
+ *   - page "LLM 推理并行化：先找瓶颈，再决定怎么切", section 三.2: the NumPy
+ *     function that, for each matched pair of shards, takes act(x @ a) @ b and sums
+ *     the partials (tanh is its default activation; mismatched shard lists are an
+ *     error);
+ *   - page "大模型推理系统揭秘（07）", section 1.4.3: the SwiGLU form
+ *     SiLU(x W1) (.) (x W3) before W2 (SiLU on the gate branch);
+ *   - page "7.4 推理侧并行", section 7.4.2 (communication quantization): partial
+ *     sums are accumulated in high precision, so partials and the reduction are fp32
+ *     by default.
+ *
+ * Conventions for every call:
+ *   - All matrices are dense, row-major, with no padding between rows.
+ *   - "_dev" pointers are device pointers (hipMalloc or torch CUDA tensors) on the
+ *     current HIP device; every other pointer is a host pointer.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued on it and the call returns without waiting, except create(), which
+ *     waits for its own work before returning.
+ *   - Calls return a status code; they never abort or throw across the ABI.
+ *     Arguments are checked on the host before anything is enqueued: a call that
+ *     returns an error has enqueued nothing.  Faults inside kernels surface at the
+ *     caller's next synchronization with the stream.
+ *   - Device pointers must be 16-byte aligned (TPM_ERR_ALIGN otherwise).
+ */
+#ifndef TP_MLP_SHARD_H
+#define TP_MLP_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tpm_status {
+  TPM_OK = 0,
+  TPM_ERR_INVALID_ARG = 1, /* NULL pointer where one is required, enum out of range */
+  TPM_ERR_SHAPE = 2,       /* size out of range or not a supported multiple */
+  TPM_ERR_ALIGN = 3,       /* a device pointer is not 16-byte aligned */
+  TPM_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  TPM_ERR_OOM = 5          /* device allocation failed */
+} tpm_status;
+
+typedef enum tpm_act {
+  TPM_ACT_TANH = 0,      /* h = tanh(X A); the default of the pages' NumPy function */
+  TPM_ACT_SILU_GATE = 1, /* h = SiLU(X G) * (X U), SiLU(x) = x / (1 + exp(-x)) */
+  TPM_ACT_IDENTITY = 2   /* h = X A */
+} tpm_act;
+
+typedef enum tpm_dtype {
+  TPM_F32 = 0,
+  TPM_BF16 = 1
+} tpm_dtype;
+
+/* Which kernels fwd uses.  AUTO picks by the token count M of each call:
+ * M <= tpm_plan_info.stream_max_tokens takes the weight-streaming path (decode),
+ * larger M the LDS-tiled matrix-core path (prefill).  The other two force a path,
+ * for any M (used to test both on the same input).  Ignored for TPM_F32 input. */
+typedef enum tpm_path {
+  TPM_PATH_AUTO = 0,
+  TPM_PATH_STREAM = 1,
+  TPM_PATH_TILED = 2
+} tpm_path;
+
+/* Shape and numerics of one rank's shard.
+ *
+ *   d_model    d: width of X, of each row of A_i and of the partial.
+ *   ffn_shard  F: hidden features held by this rank (F = ffn / TP degree).
+ *   max_tokens largest M a fwd call may pass; sizes the internal hidden buffer.
+ *   act        tpm_act.
+ *   in_dtype   dtype of X, A_i and B_i (TPM_F32 or TPM_BF16).
+ *   out_dtype  dtype of the partial written by fwd (TPM_F32 default, or TPM_BF16).
+ *   path       tpm_path.
+ *
+ * Constraints (TPM_ERR_SHAPE otherwise): d >= 1, F >= 1, max_tokens >= 0;
+ * for TPM_BF16 input d must be a multiple of 64.  F has no multiple constraint:
+ * the hidden dimension is zero-padded internally. */
+typedef struct tpm_desc {
+  int64_t d_model;
+  int64_t ffn_shard;
+  int64_t max_tokens;
+  int32_t act;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t path;
+} tpm_desc;
+
+/* What create() would allocate and how fwd would run (filled by plan()). */
+typedef struct tpm_plan_info {
+  int64_t packed_weight_bytes; /* device bytes of the handle's repacked A_i and B_i */
+  int64_t workspace_bytes;     /* device bytes of the hidden buffer and split-K scratch */
+  int64_t ffn_padded;          /* F rounded up to the internal tile width */
+  int64_t stream_max_tokens;   /* AUTO uses the streaming path for M <= this */
+  int32_t kernels_per_fwd;     /* kernel launches one fwd call makes (M > 0) */
+  int32_t reserved;
+} tpm_plan_info;
+
+typedef struct tpm_shard *tpm_shard_t;
+
+/* Status code -> static, NUL-terminated English text (never NULL). */
+const char *tpm_status_str(tpm_status status);
+
+/* Validate `desc` and report sizes, host only (no HIP call, no allocation).
+ * desc, out: host pointers, required.  On error *out is left untouched. */
+tpm_status tp_mlp_shard_plan(const tpm_desc *desc, tpm_plan_info *out);
+
+/* Create a shard handle: allocate its device memory on the current device, repack
+ * the rank's weights into the layout the kernels stream, and wait for `stream`.
+ *
+ *   A_dev  first-weight shard, [d x F] (tanh, identity) or [d x 2F] (silu_gate:
+ *          each row holds the F gate weights, then the F up weights, both over the
+ *          rank's hidden indices), dtype desc->in_dtype.
+ *   B_dev  second-weight shard, [F x d], dtype desc->in_dtype.
+ *   out    host pointer that receives the handle.
+ *
+ * The handle owns copies of the weights: A_dev and B_dev may be freed once create
+ * returns.  On error *out is set to NULL and nothing stays allocated. */
+tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const void *B_dev,
+                               void *stream, tpm_shard_t *out);
+
+/* One rank's forward: partial_dev = act(X_dev A_i) B_i.
+ *
+ *   X_dev        tokens, [M x d], dtype in_dtype.
+ *   M            token count, 0 <= M <= max_tokens; M = 0 is a successful no-op.
+ *   partial_dev  output, [M x d], dtype out_dtype, fully overwritten.
+ *
+ * Asynchronous on `stream`; allocates nothing, so it may be captured in a HIP
+ * graph.  A handle keeps per-call state (hidden buffer, split-K scratch): use one
+ * handle on one stream at a time.  X_dev and partial_dev must not overlap. */
+tpm_status tp_mlp_shard_fwd(tpm_shard_t h, const void *X_dev, int64_t M, void *partial_dev,
+                            void *stream);
+
+/* Sum k partials held on this GPU, in rank order, with fp32 accumulation:
+ *   out_dev[e] = (((p_0[e] + p_1[e]) + p_2[e]) + ...) + p_{k-1}[e],  0 <= e < numel.
+ *
+ *   partials_dev  host array of k device pointers, each to numel elements of in_dtype.
+ *   k             1 <= k <= 16 (k = 1 copies, or converts the dtype).
+ *   numel         elements per partial, >= 0 (0 is a no-op).
+ *   out_dev       numel elements of out_dtype.  It may be partials_dev[0] itself
+ *                 (same pointer, same dtype); any other overlap is undefined.
+ * The result is bitwise reproducible from call to call.  Asynchronous on `stream`. */
+tpm_status tp_partials_reduce(const void *const *partials_dev, int32_t k, int64_t numel,
+                              int32_t in_dtype, void *out_dev, int32_t out_dtype, void *stream);
+
+/* Free a handle and its device memory (waits for the device first).  NULL is OK. */
+tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
+
+/* Timing hook for profiling.  When `events` is non-NULL, every later fwd call on
+ * this handle records events[2j] on its stream just before its j-th kernel launch
+ * and events[2j+1] just after it, for j < kernels_per_fwd; n_events must be at least
+ * 2 * kernels_per_fwd.  The events are hipEvent_t created by the caller, passed as
+ * void*, and stay owned by the caller.  events = NULL (with n_events = 0) switches
+ * the hook off.  Recording events is the only thing it changes. */
+tpm_status tp_mlp_shard_set_timing_events(tpm_shard_t h, void *const *events, int32_t n_events);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* TP_MLP_SHARD_H */

@@ -1,0 +1,267 @@
+"""Python binding of ``libtpmlp.so``: the tensor-parallel MLP shard on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+of the library.  PyTorch supplies device memory and the current stream.  If the
+library is not built, every call raises; there is no CPU fallback.
+
+The functions carry the names of the C ABI (``include/tp_mlp_shard.h``):
+
+* ``tp_mlp_shard_plan``, ``tp_mlp_shard_create``, ``tp_mlp_shard_fwd``,
+  ``tp_mlp_shard_destroy``, ``tp_partials_reduce``, ``tpm_status_str``,
+  ``tp_mlp_shard_set_timing_events``;
+
+plus two conveniences: ``Shard`` (one rank's handle) and
+``tensor_parallel_output(x, a_shards, b_shards, activation="tanh")``, the pages'
+statement Z = sum_i act(x @ a_i) @ b_i (page "LLM 推理并行化：先找瓶颈，再决定怎么
+切", section 三.2), which raises ``ValueError`` when the shard lists differ in length.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
+    "tp_partials_reduce", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
+    "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+
+ACT = {"tanh": 0, "silu_gate": 1, "identity": 2}
+PATH = {"auto": 0, "stream": 1, "tiled": 2}
+F32, BF16 = 0, 1
+
+STATUS_NAMES = {0: "TPM_OK", 1: "TPM_ERR_INVALID_ARG", 2: "TPM_ERR_SHAPE", 3: "TPM_ERR_ALIGN",
+                4: "TPM_ERR_HIP", 5: "TPM_ERR_OOM"}
+
+
+class TpmDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int64), ("ffn_shard", ctypes.c_int64),
+                ("max_tokens", ctypes.c_int64), ("act", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("path", ctypes.c_int32)]
+
+
+class TpmPlanInfo(ctypes.Structure):
+    _fields_ = [("packed_weight_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("ffn_padded", ctypes.c_int64), ("stream_max_tokens", ctypes.c_int64),
+                ("kernels_per_fwd", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class TpmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS_NAMES.get(status, status),
+                                           tpm_status_str(status)))
+
+
+_lib = None
+
+
+def capi():
+    """The loaded library with its C signatures declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtpmlp.so is not built (%s); run __graft_entry__.build() "
+                           "-- there is no CPU fallback" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.tpm_status_str.argtypes = [ctypes.c_int]
+    lib.tpm_status_str.restype = ctypes.c_char_p
+    lib.tp_mlp_shard_plan.argtypes = [ctypes.POINTER(TpmDesc), ctypes.POINTER(TpmPlanInfo)]
+    lib.tp_mlp_shard_plan.restype = ctypes.c_int
+    lib.tp_mlp_shard_create.argtypes = [ctypes.POINTER(TpmDesc), vp, vp, vp, ctypes.POINTER(vp)]
+    lib.tp_mlp_shard_create.restype = ctypes.c_int
+    lib.tp_mlp_shard_fwd.argtypes = [vp, vp, i64, vp, vp]
+    lib.tp_mlp_shard_fwd.restype = ctypes.c_int
+    lib.tp_partials_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, i32, vp, i32, vp]
+    lib.tp_partials_reduce.restype = ctypes.c_int
+    lib.tp_mlp_shard_destroy.argtypes = [vp]
+    lib.tp_mlp_shard_destroy.restype = ctypes.c_int
+    lib.tp_mlp_shard_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
+    lib.tp_mlp_shard_set_timing_events.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def tpm_status_str(status: int) -> str:
+    return capi().tpm_status_str(int(status)).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise TpmError(rc, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % dt)
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _dev_ptr(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous (row-major, no padding)" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_desc(d_model, ffn_shard, max_tokens, activation="silu_gate", in_dtype=BF16,
+              out_dtype=F32, path="auto") -> TpmDesc:
+    return TpmDesc(int(d_model), int(ffn_shard), int(max_tokens), ACT[activation],
+                   int(in_dtype), int(out_dtype), PATH[path])
+
+
+def tp_mlp_shard_plan(desc: TpmDesc) -> dict:
+    info = TpmPlanInfo()
+    _check(capi().tp_mlp_shard_plan(ctypes.byref(desc), ctypes.byref(info)), "tp_mlp_shard_plan")
+    return {f: getattr(info, f) for f, _ in TpmPlanInfo._fields_ if f != "reserved"}
+
+
+def tp_mlp_shard_create(desc: TpmDesc, A, B, stream=None) -> int:
+    """Create a shard handle from device tensors A [d, F or 2F] and B [F, d]."""
+    h = ctypes.c_void_p()
+    _check(capi().tp_mlp_shard_create(ctypes.byref(desc), _dev_ptr(A, "A"), _dev_ptr(B, "B"),
+                                      _stream_ptr(stream), ctypes.byref(h)), "tp_mlp_shard_create")
+    return h.value
+
+
+def tp_mlp_shard_fwd(handle: int, X, M: int, partial, stream=None) -> None:
+    _check(capi().tp_mlp_shard_fwd(ctypes.c_void_p(handle), _dev_ptr(X, "X"), int(M),
+                                   _dev_ptr(partial, "partial"), _stream_ptr(stream)),
+           "tp_mlp_shard_fwd")
+
+
+def tp_partials_reduce(partials, out, stream=None) -> None:
+    """out = sum of the partials (rank order, fp32 accumulation)."""
+    parts = list(partials)
+    if not parts:
+        raise ValueError("need at least one partial")
+    numel = parts[0].numel()
+    in_dt = parts[0].dtype
+    for p in parts:
+        if p.numel() != numel or p.dtype != in_dt:
+            raise ValueError("partials must agree in size and dtype")
+    if out.numel() != numel:
+        raise ValueError("out has %d elements, partials %d" % (out.numel(), numel))
+    arr = (ctypes.c_void_p * len(parts))(*[_dev_ptr(p, "partial").value for p in parts])
+    _check(capi().tp_partials_reduce(arr, len(parts), numel, _dtype_code(in_dt),
+                                     _dev_ptr(out, "out"), _dtype_code(out.dtype),
+                                     _stream_ptr(stream)), "tp_partials_reduce")
+
+
+def tp_mlp_shard_destroy(handle: int) -> None:
+    _check(capi().tp_mlp_shard_destroy(ctypes.c_void_p(handle)), "tp_mlp_shard_destroy")
+
+
+def tp_mlp_shard_set_timing_events(handle: int, events) -> None:
+    """events: sequence of raw hipEvent_t values (ints), or None to switch off."""
+    if events is None:
+        _check(capi().tp_mlp_shard_set_timing_events(ctypes.c_void_p(handle), None, 0),
+               "tp_mlp_shard_set_timing_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
+    _check(capi().tp_mlp_shard_set_timing_events(ctypes.c_void_p(handle), arr, len(events)),
+           "tp_mlp_shard_set_timing_events")
+
+
+class Shard:
+    """One rank's shard: owns a library handle with repacked weights.
+
+    a: first-weight shard [d, F] (tanh, identity) or [d, 2F] (silu_gate: F gate
+       columns then F up columns), b: second-weight shard [F, d]; both GPU tensors
+       of the same dtype (float32 or bfloat16)."""
+
+    def __init__(self, a, b, activation="tanh", max_tokens=None, out_dtype=None, path="auto",
+                 stream=None):
+        torch = _torch()
+        if a.dim() != 2 or b.dim() != 2:
+            raise ValueError("a and b must be 2-D")
+        if a.dtype != b.dtype:
+            raise ValueError("a and b must share a dtype")
+        d, F = a.shape[0], b.shape[0]
+        ncol = 2 * F if activation == "silu_gate" else F
+        if a.shape[1] != ncol or b.shape[1] != d:
+            raise ValueError("shard shapes %s, %s do not fit activation %s"
+                             % (tuple(a.shape), tuple(b.shape), activation))
+        self.d_model, self.ffn_shard, self.activation = d, F, activation
+        self.in_dtype = a.dtype
+        self.out_dtype = out_dtype if out_dtype is not None else torch.float32
+        self.max_tokens = int(max_tokens) if max_tokens is not None else 8192
+        self.desc = make_desc(d, F, self.max_tokens, activation, _dtype_code(a.dtype),
+                              _dtype_code(self.out_dtype), path)
+        self.plan = tp_mlp_shard_plan(self.desc)
+        self.handle = tp_mlp_shard_create(self.desc, a, b, stream)
+
+    def forward(self, x, out=None, stream=None):
+        torch = _torch()
+        if x.dim() != 2 or x.shape[1] != self.d_model or x.dtype != self.in_dtype:
+            raise ValueError("x must be [M, %d] of %s" % (self.d_model, self.in_dtype))
+        M = x.shape[0]
+        if out is None:
+            out = torch.empty((M, self.d_model), dtype=self.out_dtype, device=x.device)
+        elif out.shape != (M, self.d_model) or out.dtype != self.out_dtype:
+            raise ValueError("out must be [M, d] of %s" % self.out_dtype)
+        tp_mlp_shard_fwd(self.handle, x, M, out, stream)
+        return out
+
+    __call__ = forward
+
+    def set_timing_events(self, events):
+        tp_mlp_shard_set_timing_events(self.handle, events)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            tp_mlp_shard_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def partials_reduce(partials, out=None, out_dtype=None, stream=None):
+    torch = _torch()
+    parts = list(partials)
+    if out is None:
+        out = torch.empty_like(parts[0], dtype=out_dtype or torch.float32)
+    tp_partials_reduce(parts, out, stream)
+    return out
+
+
+def tensor_parallel_output(x, a_shards, b_shards, activation="tanh", path="auto",
+                           out_dtype=None):
+    """Z = sum_i act(x @ a_i) @ b_i over matched shard pairs, all on the GPU."""
+    a_shards, b_shards = list(a_shards), list(b_shards)
+    if len(a_shards) != len(b_shards):
+        raise ValueError("a_shards and b_shards differ in count (%d vs %d)"
+                         % (len(a_shards), len(b_shards)))
+    shards = [Shard(a, b, activation, max_tokens=x.shape[0], path=path) for a, b in
+              zip(a_shards, b_shards)]
+    try:
+        partials = [s.forward(x) for s in shards]
+        return partials_reduce(partials, out_dtype=out_dtype)
+    finally:
+        for s in shards:
+            s.close()

@@ -1,0 +1,305 @@
+// C ABI of libtpmlp: argument checks, handle lifetime, kernel choice.
+//
+// Every argument is checked on the host before anything is enqueued, so a call
+// that fails has no effect on the device.  fwd makes exactly two launches (first
+// projection with its fused activation, then the second projection), allocates
+// nothing and never synchronizes, so it can be captured in a HIP graph.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "tpm_internal.h"
+
+using namespace tpm;
+
+namespace {
+
+constexpr int64_t kAlign = 16;
+constexpr int64_t kSubAlign = 256;
+constexpr int kMaxParts = 16;
+
+bool aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+tpm_status check_desc(const tpm_desc *d) {
+  if (!d) return TPM_ERR_INVALID_ARG;
+  if (d->act < TPM_ACT_TANH || d->act > TPM_ACT_IDENTITY) return TPM_ERR_INVALID_ARG;
+  if (d->in_dtype != TPM_F32 && d->in_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (d->out_dtype != TPM_F32 && d->out_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (d->path < TPM_PATH_AUTO || d->path > TPM_PATH_TILED) return TPM_ERR_INVALID_ARG;
+  if (d->d_model < 1 || d->ffn_shard < 1 || d->max_tokens < 0) return TPM_ERR_SHAPE;
+  // Keep every index the kernels form inside 32-bit ints and every size sane.
+  if (d->d_model > (int64_t(1) << 20) || d->ffn_shard > (int64_t(1) << 20) ||
+      d->max_tokens > (int64_t(1) << 24))
+    return TPM_ERR_SHAPE;
+  if (d->in_dtype == TPM_BF16 && d->d_model % 64 != 0) return TPM_ERR_SHAPE;
+  return TPM_OK;
+}
+
+int first_epi(int act) {
+  return act == TPM_ACT_SILU_GATE ? EPI_SILU_GATE : act == TPM_ACT_TANH ? EPI_TANH : EPI_IDENTITY;
+}
+
+tpm_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return TPM_OK;
+  if (e == hipErrorOutOfMemory) return TPM_ERR_OOM;
+  return TPM_ERR_HIP;
+}
+
+}  // namespace
+
+namespace tpm {
+
+Sizes compute_sizes(const tpm_desc &d) {
+  Sizes z = {};
+  const int64_t F = d.ffn_shard, D = d.d_model;
+  const bool silu = d.act == TPM_ACT_SILU_GATE;
+  if (d.in_dtype == TPM_BF16) {
+    z.ffn_pad = silu ? round_up(F, kTileN / 2) : round_up(F, kTileN);
+    z.n1 = silu ? 2 * z.ffn_pad : z.ffn_pad;
+    z.n2 = round_up(D, kTileN);
+    z.w1_bytes = z.n1 * D * 2;
+    z.w2_bytes = z.n2 * z.ffn_pad * 2;
+    z.hidden_bytes = d.max_tokens * z.ffn_pad * 2;
+    // Split-K scratch for the streaming path (only used when all tokens fit one
+    // group of 64 rows); the two projections run one after the other and share it.
+    const int ncb1 = silu ? 2 : 1;
+    const int64_t units1 = z.n1 / kFragN / ncb1, units2 = z.n2 / kFragN;
+    const StreamCfg c1 = stream_config(kStreamMaxTokens, units1, D / kFragK);
+    const StreamCfg c2 = stream_config(kStreamMaxTokens, units2, z.ffn_pad / kFragK);
+    const int64_t f1 = c1.ksplit > 1 ? units1 * c1.ksplit * 2 * ncb1 * 16 * 64 : 0;
+    const int64_t f2 = c2.ksplit > 1 ? units2 * c2.ksplit * 2 * 16 * 64 : 0;
+    z.splitk_floats = f1 > f2 ? f1 : f2;
+    z.n_counters = units1 > units2 ? units1 : units2;
+  } else {
+    z.ffn_pad = F;
+    z.n1 = silu ? 2 * F : F;
+    z.n2 = D;
+    z.w1_bytes = z.n1 * D * 4;
+    z.w2_bytes = F * D * 4;
+    z.hidden_bytes = d.max_tokens * F * 4;
+  }
+  return z;
+}
+
+}  // namespace tpm
+
+extern "C" {
+
+const char *tpm_status_str(tpm_status s) {
+  switch (s) {
+    case TPM_OK: return "ok";
+    case TPM_ERR_INVALID_ARG: return "invalid argument (null pointer or enum out of range)";
+    case TPM_ERR_SHAPE: return "unsupported shape or size out of range";
+    case TPM_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case TPM_ERR_HIP: return "HIP runtime error";
+    case TPM_ERR_OOM: return "device out of memory";
+    default: return "unknown status";
+  }
+}
+
+tpm_status tp_mlp_shard_plan(const tpm_desc *desc, tpm_plan_info *out) {
+  if (!out) return TPM_ERR_INVALID_ARG;
+  const tpm_status st = check_desc(desc);
+  if (st != TPM_OK) return st;
+  const Sizes z = compute_sizes(*desc);
+  tpm_plan_info info = {};
+  info.packed_weight_bytes = z.w1_bytes + z.w2_bytes;
+  info.workspace_bytes = z.hidden_bytes + z.splitk_floats * 4 + z.n_counters * 4;
+  info.ffn_padded = z.ffn_pad;
+  info.stream_max_tokens = desc->in_dtype == TPM_BF16 ? kStreamMaxTokens : 0;
+  info.kernels_per_fwd = 2;
+  *out = info;
+  return TPM_OK;
+}
+
+tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const void *B_dev,
+                               void *stream, tpm_shard_t *out) {
+  if (!out) return TPM_ERR_INVALID_ARG;
+  *out = nullptr;
+  tpm_status st = check_desc(desc);
+  if (st != TPM_OK) return st;
+  if (!A_dev || !B_dev) return TPM_ERR_INVALID_ARG;
+  if (!aligned(A_dev) || !aligned(B_dev)) return TPM_ERR_ALIGN;
+
+  const tpm_desc d = *desc;
+  const Sizes z = compute_sizes(d);
+  Shard *h = new (std::nothrow) Shard();
+  if (!h) return TPM_ERR_OOM;
+  h->desc = d;
+  h->ffn_pad = z.ffn_pad;
+  h->n1 = z.n1;
+  h->n2 = z.n2;
+  h->k1_blocks = d.d_model / kFragK;
+  h->k2_blocks = z.ffn_pad / kFragK;
+  h->splitk_floats = z.splitk_floats;
+  h->n_counters = z.n_counters;
+  h->n_events = 0;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return from_hip(e);
+  }
+  const int64_t o_w1 = 0;
+  const int64_t o_w2 = round_up(o_w1 + z.w1_bytes, kSubAlign);
+  const int64_t o_hid = round_up(o_w2 + z.w2_bytes, kSubAlign);
+  const int64_t o_sk = round_up(o_hid + z.hidden_bytes, kSubAlign);
+  const int64_t o_cnt = round_up(o_sk + z.splitk_floats * 4, kSubAlign);
+  const int64_t total = round_up(o_cnt + z.n_counters * 4, kSubAlign);
+  e = hipMalloc(&h->alloc_base, static_cast<size_t>(total));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return TPM_ERR_OOM;
+  }
+  char *base = static_cast<char *>(h->alloc_base);
+  h->alloc_bytes = total;
+  h->w1 = base + o_w1;
+  h->w2 = base + o_w2;
+  h->hidden = z.hidden_bytes ? base + o_hid : nullptr;
+  h->splitk = z.splitk_floats ? reinterpret_cast<float *>(base + o_sk) : nullptr;
+  h->counters = z.n_counters ? reinterpret_cast<int *>(base + o_cnt) : nullptr;
+
+  const bool silu = d.act == TPM_ACT_SILU_GATE;
+  const int64_t a_cols = silu ? 2 * d.ffn_shard : d.ffn_shard;
+  if (d.in_dtype == TPM_BF16) {
+    e = launch_pack_bf16(A_dev, a_cols, d.d_model, a_cols, silu, d.ffn_shard, z.n1 / kFragN,
+                         h->k1_blocks, h->w1, s);
+    if (e == hipSuccess)
+      e = launch_pack_bf16(B_dev, d.d_model, d.ffn_shard, d.d_model, false, d.ffn_shard,
+                           z.n2 / kFragN, h->k2_blocks, h->w2, s);
+    if (e == hipSuccess && h->counters)
+      e = hipMemsetAsync(h->counters, 0, static_cast<size_t>(z.n_counters * 4), s);
+  } else {
+    e = hipMemcpyAsync(h->w1, A_dev, static_cast<size_t>(z.w1_bytes), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h->w2, B_dev, static_cast<size_t>(z.w2_bytes), hipMemcpyDeviceToDevice, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(h->alloc_base);
+    delete h;
+    return from_hip(e);
+  }
+  *out = reinterpret_cast<tpm_shard_t>(h);
+  return TPM_OK;
+}
+
+tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, void *partial_dev,
+                            void *stream) {
+  Shard *h = reinterpret_cast<Shard *>(handle);
+  if (!h) return TPM_ERR_INVALID_ARG;
+  const tpm_desc &d = h->desc;
+  if (M < 0 || M > d.max_tokens) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X_dev || !partial_dev) return TPM_ERR_INVALID_ARG;
+  if (!aligned(X_dev) || !aligned(partial_dev)) return TPM_ERR_ALIGN;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return TPM_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int epi1 = first_epi(d.act);
+  const int epi2 = d.out_dtype == TPM_F32 ? EPI_OUT_F32 : EPI_OUT_BF16;
+  const bool ev = h->n_events >= 4;
+  hipError_t e = hipSuccess;
+  auto rec = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord(h->events[i], s);
+  };
+
+  if (d.in_dtype == TPM_F32) {
+    const int64_t a_cols = d.act == TPM_ACT_SILU_GATE ? 2 * d.ffn_shard : d.ffn_shard;
+    rec(0);
+    if (e == hipSuccess)
+      e = launch_f32_gemm(epi1, static_cast<const float *>(X_dev), d.d_model, M, d.d_model,
+                          static_cast<const float *>(h->w1), a_cols, d.ffn_shard, d.ffn_shard,
+                          h->hidden, d.ffn_shard, s);
+    rec(1);
+    rec(2);
+    if (e == hipSuccess)
+      e = launch_f32_gemm(epi2, static_cast<const float *>(h->hidden), d.ffn_shard, M,
+                          d.ffn_shard, static_cast<const float *>(h->w2), d.d_model, d.d_model, 0,
+                          partial_dev, d.d_model, s);
+    rec(3);
+    return from_hip(e);
+  }
+
+  int path = d.path;
+  if (path == TPM_PATH_AUTO) path = M <= kStreamMaxTokens ? TPM_PATH_STREAM : TPM_PATH_TILED;
+  rec(0);
+  if (e == hipSuccess) {
+    if (path == TPM_PATH_STREAM) {
+      const int64_t units1 = h->n1 / kFragN / (d.act == TPM_ACT_SILU_GATE ? 2 : 1);
+      const StreamCfg c1 = stream_config(M, units1, h->k1_blocks);
+      e = launch_stream_gemm(epi1, X_dev, d.d_model, M, h->k1_blocks, h->w1, c1, h->hidden,
+                             h->ffn_pad, h->ffn_pad, h->splitk, h->counters, s);
+    } else {
+      e = launch_tiled_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden,
+                            h->ffn_pad, h->ffn_pad, s);
+    }
+  }
+  rec(1);
+  rec(2);
+  if (e == hipSuccess) {
+    if (path == TPM_PATH_STREAM) {
+      const StreamCfg c2 = stream_config(M, h->n2 / kFragN, h->k2_blocks);
+      e = launch_stream_gemm(epi2, h->hidden, h->ffn_pad, M, h->k2_blocks, h->w2, c2, partial_dev,
+                             d.d_model, d.d_model, h->splitk, h->counters, s);
+    } else {
+      e = launch_tiled_gemm(epi2, h->hidden, h->ffn_pad, M, h->ffn_pad, h->w2, h->n2, partial_dev,
+                            d.d_model, d.d_model, s);
+    }
+  }
+  rec(3);
+  return from_hip(e);
+}
+
+tpm_status tp_partials_reduce(const void *const *partials_dev, int32_t k, int64_t numel,
+                              int32_t in_dtype, void *out_dev, int32_t out_dtype, void *stream) {
+  if (!partials_dev || !out_dev) return TPM_ERR_INVALID_ARG;
+  if (in_dtype != TPM_F32 && in_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (out_dtype != TPM_F32 && out_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxParts || numel < 0) return TPM_ERR_SHAPE;
+  for (int i = 0; i < k; ++i) {
+    if (!partials_dev[i]) return TPM_ERR_INVALID_ARG;
+    if (!aligned(partials_dev[i])) return TPM_ERR_ALIGN;
+  }
+  if (!aligned(out_dev)) return TPM_ERR_ALIGN;
+  if (out_dev == partials_dev[0] && in_dtype != out_dtype) return TPM_ERR_INVALID_ARG;
+  if (numel == 0) return TPM_OK;
+  return from_hip(launch_reduce(partials_dev, k, numel, in_dtype, out_dev, out_dtype,
+                                static_cast<hipStream_t>(stream)));
+}
+
+tpm_status tp_mlp_shard_destroy(tpm_shard_t handle) {
+  Shard *h = reinterpret_cast<Shard *>(handle);
+  if (!h) return TPM_OK;
+  hipError_t e = hipDeviceSynchronize();
+  const hipError_t e2 = hipFree(h->alloc_base);
+  if (e == hipSuccess) e = e2;
+  delete h;
+  return from_hip(e);
+}
+
+tpm_status tp_mlp_shard_set_timing_events(tpm_shard_t handle, void *const *events,
+                                          int32_t n_events) {
+  Shard *h = reinterpret_cast<Shard *>(handle);
+  if (!h) return TPM_ERR_INVALID_ARG;
+  if (!events) {
+    if (n_events != 0) return TPM_ERR_INVALID_ARG;
+    h->n_events = 0;
+    return TPM_OK;
+  }
+  if (n_events < 4) return TPM_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i) {
+    if (!events[i]) return TPM_ERR_INVALID_ARG;
+    h->events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  h->n_events = 4;
+  return TPM_OK;
+}
+
+}  // extern "C"

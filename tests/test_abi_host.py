@@ -1,0 +1,148 @@
+"""The C ABI on the host: the library loads, exports what the header declares, and
+rejects bad arguments before touching the device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_mlp_shard_amd as tpm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp_shard.h")
+
+OK, INVALID, SHAPE, ALIGN = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tpm.LIB_PATH):
+        from tensor_mlp_shard_amd import build
+        build.build()
+    return tpm.capi()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_\w+|tpm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd",
+              "tp_partials_reduce", "tp_mlp_shard_destroy", "tpm_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert tpm.tpm_status_str(s)
+    assert tpm.tpm_status_str(99) == "unknown status"
+
+
+def desc(**kw):
+    base = dict(d_model=8192, ffn_shard=3584, max_tokens=8192, activation="silu_gate",
+                in_dtype=tpm.BF16, out_dtype=tpm.F32, path="auto")
+    base.update(kw)
+    return tpm.make_desc(**base)
+
+
+def plan_rc(d):
+    info = tpm.TpmPlanInfo()
+    return tpm.capi().tp_mlp_shard_plan(ctypes.byref(d), ctypes.byref(info)), info
+
+
+def test_plan_decode_shard_sizes(lib):
+    p = tpm.tp_mlp_shard_plan(desc())
+    assert p["packed_weight_bytes"] == 8192 * 7168 * 2 + 8192 * 3584 * 2
+    assert p["ffn_padded"] == 3584
+    assert p["stream_max_tokens"] == 64 and p["kernels_per_fwd"] == 2
+    assert p["workspace_bytes"] >= 8192 * 3584 * 2
+
+
+def test_plan_pads_ragged_ffn(lib):
+    p = tpm.tp_mlp_shard_plan(desc(d_model=512, ffn_shard=200, activation="tanh"))
+    assert p["ffn_padded"] == 256
+    p = tpm.tp_mlp_shard_plan(desc(d_model=512, ffn_shard=200, activation="silu_gate"))
+    assert p["ffn_padded"] == 256
+    p = tpm.tp_mlp_shard_plan(desc(d_model=64, ffn_shard=7, in_dtype=tpm.F32, activation="tanh"))
+    assert p["ffn_padded"] == 7 and p["stream_max_tokens"] == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_model=0), SHAPE), (dict(ffn_shard=0), SHAPE), (dict(max_tokens=-1), SHAPE),
+    (dict(d_model=8200), SHAPE),  # bf16 needs d % 64 == 0
+    (dict(d_model=8200, in_dtype=tpm.F32), OK),
+    (dict(in_dtype=7), INVALID), (dict(out_dtype=-1), INVALID),
+    (dict(d_model=1 << 21), SHAPE),
+])
+def test_plan_validation(lib, kw, code):
+    rc, _ = plan_rc(desc(**kw))
+    assert rc == code
+
+
+def test_plan_rejects_bad_enums_and_nulls(lib):
+    d = desc()
+    d.act = 3
+    assert plan_rc(d)[0] == INVALID
+    d = desc()
+    d.path = 9
+    assert plan_rc(d)[0] == INVALID
+    info = tpm.TpmPlanInfo()
+    assert lib.tp_mlp_shard_plan(None, ctypes.byref(info)) == INVALID
+    assert lib.tp_mlp_shard_plan(ctypes.byref(desc()), None) == INVALID
+
+
+def test_create_rejects_before_any_device_work(lib):
+    h = ctypes.c_void_p(1234)
+    d = desc()
+    assert lib.tp_mlp_shard_create(ctypes.byref(d), None, None, None, ctypes.byref(h)) == INVALID
+    assert h.value is None  # out is cleared on error
+    assert lib.tp_mlp_shard_create(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                                   ctypes.c_void_p(0x1008), None, ctypes.byref(h)) == ALIGN
+    bad = desc(d_model=100)
+    assert lib.tp_mlp_shard_create(ctypes.byref(bad), ctypes.c_void_p(0x1000),
+                                   ctypes.c_void_p(0x2000), None, ctypes.byref(h)) == SHAPE
+    assert lib.tp_mlp_shard_create(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                                   ctypes.c_void_p(0x2000), None, None) == INVALID
+
+
+def test_fwd_and_destroy_null_handle(lib):
+    assert lib.tp_mlp_shard_fwd(None, ctypes.c_void_p(0x1000), 4, ctypes.c_void_p(0x2000),
+                                None) == INVALID
+    assert lib.tp_mlp_shard_destroy(None) == OK
+    assert lib.tp_mlp_shard_set_timing_events(None, None, 0) == INVALID
+
+
+def _ptrs(*vals):
+    return (ctypes.c_void_p * len(vals))(*vals)
+
+
+def test_reduce_validation(lib):
+    p = _ptrs(0x1000, 0x2000)
+    out = ctypes.c_void_p(0x3000)
+    assert lib.tp_partials_reduce(None, 2, 16, 0, out, 0, None) == INVALID
+    assert lib.tp_partials_reduce(p, 2, 16, 0, None, 0, None) == INVALID
+    assert lib.tp_partials_reduce(p, 0, 16, 0, out, 0, None) == SHAPE
+    assert lib.tp_partials_reduce(_ptrs(*([0x1000] * 17)), 17, 16, 0, out, 0, None) == SHAPE
+    assert lib.tp_partials_reduce(p, 2, -1, 0, out, 0, None) == SHAPE
+    assert lib.tp_partials_reduce(p, 2, 16, 5, out, 0, None) == INVALID
+    assert lib.tp_partials_reduce(p, 2, 16, 0, out, 5, None) == INVALID
+    assert lib.tp_partials_reduce(_ptrs(0x1000, None), 2, 16, 0, out, 0, None) == INVALID
+    assert lib.tp_partials_reduce(_ptrs(0x1000, 0x2004), 2, 16, 0, out, 0, None) == ALIGN
+    assert lib.tp_partials_reduce(p, 2, 16, 0, ctypes.c_void_p(0x3002), 0, None) == ALIGN
+    # in-place needs the same dtype
+    assert lib.tp_partials_reduce(p, 2, 16, 0, ctypes.c_void_p(0x1000), 1, None) == INVALID
+    # numel = 0 is a no-op that never touches the device
+    assert lib.tp_partials_reduce(p, 2, 0, 0, out, 0, None) == OK
+
+
+def test_python_wrapper_shard_count_mismatch():
+    with pytest.raises(ValueError):
+        tpm.tensor_parallel_output(None, [1, 2], [1])
