@@ -1,0 +1,349 @@
+"""Throughput of the tensor-parallel MLP shard forward on one MI355X.
+
+One step is one pass of the whole per-layer path at the decode shape of a
+70B-class MLP (d_model 8192, ffn 28672, SwiGLU, bf16 weights N(0, 0.02), tokens
+N(0, 1)): the eight rank shards of tensor-parallel degree 8 (per-rank hidden width
+3584, M = 32 tokens) are computed one after another on the GPU, each a
+``tp_mlp_shard_fwd`` call (gate/up projection with the fused SiLU-gate epilogue,
+then the down projection into an fp32 partial), and ``tp_partials_reduce`` sums the
+eight partials.  The eight shards hold 1.41 GB of distinct weights, more than the
+256 MB last-level cache, so every step streams its weights from HBM.
+
+``value`` is decode weight bandwidth: bf16 weight bytes per step / time per step.
+The JSON line also carries
+
+* ``roofline``: the dominant kernel (the gate/up projection, 2/3 of the weight
+  bytes) timed by HIP events that the library records on the launch stream around
+  every launch in the timed region, against the 8 TB/s HBM peak;
+* ``prefill``: one rank shard at the prefill shape (M = 8192), TFLOP/s against the
+  2.5 PFLOP/s dense bf16 matrix-core peak, with its own per-kernel event timing;
+* ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
+  same decode workload.
+
+Inputs are seeded synthetic tensors (torch CPU generator), copied to the GPU
+before the timed region.  Usage: ``python bench.py [--steps K] [--warmup W]``.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix cores, published
+D_MODEL, FFN, TP, M_DECODE, M_PREFILL = 8192, 28672, 8, 32, 8192
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources and build flags, to tell whether stored counter
+    readings still describe the kernels that are built."""
+    from tensor_mlp_shard_amd import build as b
+    h = hashlib.sha256()
+    for src in sorted(b.SOURCES) + ["device_common.h", "tpm_internal.h"]:
+        with open(os.path.join(b.CSRC, src), "rb") as f:
+            h.update(src.encode() + b"\0" + f.read())
+    h.update(" ".join(b.HIP_FLAGS[:-1]).encode())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None if
+    there is none or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+class Rank:
+    """One rank's shard handle plus the raw C arguments of its fwd call."""
+
+    def __init__(self, tpm, lib, a, b, x, max_tokens, stream_ptr):
+        import torch
+        self.shard = tpm.Shard(a, b, "silu_gate", max_tokens=max_tokens)
+        self.out = torch.empty((x.shape[0], D_MODEL), dtype=torch.float32, device=x.device)
+        self.args = (ctypes.c_void_p(self.shard.handle), ctypes.c_void_p(x.data_ptr()),
+                     ctypes.c_int64(x.shape[0]), ctypes.c_void_p(self.out.data_ptr()), stream_ptr)
+        self.lib = lib
+
+    def fwd(self):
+        rc = self.lib.tp_mlp_shard_fwd(*self.args)
+        if rc:
+            raise RuntimeError("tp_mlp_shard_fwd failed: %d" % rc)
+
+
+class EventPool:
+    """Pre-created timing events, handed to the library's timing hook one call at a
+    time; durations are read after the timed region."""
+
+    def __init__(self, n):
+        import torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.ev:
+            e.record()
+        torch.cuda.synchronize()
+        self.raw = [ctypes.c_void_p(int(e.cuda_event)) for e in self.ev]
+        self.next = 0
+
+    def take4(self):
+        i = self.next
+        self.next += 4
+        return (ctypes.c_void_p * 4)(*self.raw[i:i + 4]), self.ev[i:i + 4]
+
+
+def decode_workload(tpm, lib, synth, dev, stream_ptr):
+    import torch
+    spec = synth.ModelSpec()
+    log("drawing the 70B-class model shards (TP=8) ...")
+    a_sh, b_sh = spec.shards(TP)
+    x_cpu = synth.tokens(M_DECODE)
+    x = x_cpu.to(dev)
+    ranks = []
+    for a, b in zip(a_sh, b_sh):
+        ranks.append(Rank(tpm, lib, a.to(dev), b.to(dev), x, M_DECODE, stream_ptr))
+    torch.cuda.synchronize()
+    z = torch.empty((M_DECODE, D_MODEL), dtype=torch.float32, device=dev)
+    parts = (ctypes.c_void_p * TP)(*[r.out.data_ptr() for r in ranks])
+    red_args = (parts, ctypes.c_int32(TP), ctypes.c_int64(M_DECODE * D_MODEL), ctypes.c_int32(0),
+                ctypes.c_void_p(z.data_ptr()), ctypes.c_int32(0), stream_ptr)
+    return ranks, red_args, z, (x_cpu, a_sh, b_sh)
+
+
+def run_decode(lib, ranks, red_args, steps, warmup):
+    import torch
+
+    def step(hooks=None):
+        for i, r in enumerate(ranks):
+            if hooks is not None:
+                arr, _ = hooks[i]
+                lib.tp_mlp_shard_set_timing_events(r.args[0], arr, 4)
+            r.fwd()
+        rc = lib.tp_partials_reduce(*red_args)
+        if rc:
+            raise RuntimeError("tp_partials_reduce failed: %d" % rc)
+
+    for _ in range(warmup):
+        step()
+    pool = EventPool(4 * len(ranks) * steps)
+    hooks = [[pool.take4() for _ in ranks] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(hooks[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for r in ranks:
+        lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
+    k1 = [evs[0].elapsed_time(evs[1]) for per_step in hooks for _, evs in per_step]
+    k2 = [evs[2].elapsed_time(evs[3]) for per_step in hooks for _, evs in per_step]
+    return (t1 - t0), k1, k2
+
+
+def run_prefill(tpm, lib, synth, dev, stream_ptr, iters, warmup):
+    import torch
+    a, b = synth.ModelSpec().shard(0, TP)
+    x = synth.tokens(M_PREFILL).to(dev)
+    r = Rank(tpm, lib, a.to(dev), b.to(dev), x, M_PREFILL, stream_ptr)
+    del a, b
+    for _ in range(warmup):
+        r.fwd()
+    pool = EventPool(4 * iters)
+    hooks = [pool.take4() for _ in range(iters)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for arr, _ in hooks:
+        lib.tp_mlp_shard_set_timing_events(r.args[0], arr, 4)
+        r.fwd()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
+    k1 = [e[0].elapsed_time(e[1]) for _, e in hooks]
+    k2 = [e[2].elapsed_time(e[3]) for _, e in hooks]
+    r.shard.close()
+    return (t1 - t0) / iters, k1, k2
+
+
+def cpu_baseline(host_inputs, budget_s=12.0):
+    """The fp64 oracle on the host over whole decode steps (8 shards at M = 32 plus
+    the partials sum) until about `budget_s` seconds of oracle compute have run."""
+    import numpy as np
+    import oracle
+    x, a_sh, b_sh = host_inputs
+    X = oracle._f64(x)
+    widened = [(oracle._f64(a), oracle._f64(b)) for a, b in zip(a_sh, b_sh)]
+    t_total, shards_done, steps_done = 0.0, 0, 0
+    while True:
+        parts = []
+        for A, B in widened:
+            P, dt = oracle.timed_shard_forward(X, A, B, "silu_gate")
+            parts.append(P)
+            t_total += dt
+            shards_done += 1
+        t0 = time.perf_counter()
+        oracle.partials_sum(parts)
+        t_total += time.perf_counter() - t0
+        steps_done += 1
+        if t_total >= budget_s or steps_done >= 8:
+            break
+    weight_bytes = sum(a.shape[0] * a.shape[1] * 2 + b.shape[0] * b.shape[1] * 2
+                       for a, b in zip(a_sh, b_sh))
+    per_step = t_total / steps_done
+    return {"value": round(weight_bytes / per_step / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d whole decode step(s): 8 TP=8 rank shards at M=32 + partials sum, "
+                      "fp64, %.1f s of oracle compute" % (steps_done, t_total),
+            "s_per_step": round(per_step, 4)}
+
+
+def calib_copy(dev, nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("calibration copy: %d bytes read, %d bytes written, %d times" % (nbytes, nbytes, reps))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no cross-GPU path (no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tensor_mlp_shard_amd as tpm
+    from tensor_mlp_shard_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib = tpm.capi()  # raises if libtpmlp.so is not built: there is no fallback
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream_ptr = ctypes.c_void_p(int(torch.cuda.current_stream().cuda_stream))
+    props = torch.cuda.get_device_properties(dev)
+    log("device:", props.name, "CUs:", props.multi_processor_count)
+
+    ranks, red_args, _, host_inputs = decode_workload(tpm, lib, synth, dev, stream_ptr)
+    w_bytes_rank = D_MODEL * 2 * (FFN // TP) * 2 + (FFN // TP) * D_MODEL * 2
+    w_bytes_step = TP * w_bytes_rank
+    log("decode: %d steps (warmup %d) ..." % (args.steps, args.warmup))
+    elapsed, k1, k2 = run_decode(lib, ranks, red_args, args.steps, args.warmup)
+    ms_step = elapsed / args.steps * 1e3
+    value = w_bytes_step / (elapsed / args.steps) / 1e9
+
+    F = FFN // TP
+    k1_bytes = D_MODEL * 2 * F * 2 + M_DECODE * D_MODEL * 2 + M_DECODE * F * 2
+    k2_bytes = F * D_MODEL * 2 + M_DECODE * F * 2 + M_DECODE * D_MODEL * 4
+    k1_ms = sum(k1) / len(k1)
+    k2_ms = sum(k2) / len(k2)
+    achieved = k1_bytes / (k1_ms * 1e-3) / 1e9
+    traffic = stored_traffic("gate_up_decode")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "k_stream<SILU_GATE> (gate/up projection, decode shard M=32)",
+                "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
+                "launches": len(k1)}
+    down = {"kernel": "k_stream<OUT_F32> (down projection, decode shard M=32)",
+            "algorithmic_bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2),
+            "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)}
+    shard_us = (k1_ms + k2_ms) * 1e3
+    shard_bytes = w_bytes_rank + M_DECODE * D_MODEL * 2 + M_DECODE * D_MODEL * 4
+    log("decode: %.3f ms/step, %.1f GB/s weights; gate/up %.2f us, down %.2f us"
+        % (ms_step, value, k1_ms * 1e3, k2_ms * 1e3))
+
+    prefill = None
+    if not args.no_prefill:
+        for r in ranks:
+            r.shard.close()
+        ranks = None
+        torch.cuda.empty_cache()
+        log("prefill: %d iterations ..." % args.prefill_iters)
+        t_call, p1, p2 = run_prefill(tpm, lib, synth, dev, stream_ptr, args.prefill_iters, 3)
+        flops1 = 2 * M_PREFILL * D_MODEL * 2 * F
+        flops2 = 2 * M_PREFILL * F * D_MODEL
+        p1_ms, p2_ms = sum(p1) / len(p1), sum(p2) / len(p2)
+        tf = (flops1 + flops2) / t_call / 1e12
+        prefill = {"metric": "prefill shard TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
+                   "ms_per_call": round(t_call * 1e3, 4),
+                   "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                   "config": {"workload": "prefill shard: one TP=8 rank, d_model 8192, F 3584, "
+                                          "SwiGLU, X [8192 x 8192] bf16"},
+                   "roofline": {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "kernel": "k_tiled<SILU_GATE> (gate/up projection)",
+                                "achieved": round(flops1 / (p1_ms * 1e-3) / 1e12, 1),
+                                "frac": round(flops1 / (p1_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                                "avg_launch_us": round(p1_ms * 1e3, 1),
+                                "traffic": stored_traffic("gate_up_prefill")},
+                   "down": {"kernel": "k_tiled<OUT_F32> (down projection)",
+                            "achieved_TFLOPs": round(flops2 / (p2_ms * 1e-3) / 1e12, 1),
+                            "avg_launch_us": round(p2_ms * 1e3, 1)}}
+        log("prefill: %.3f ms/call, %.1f TFLOP/s" % (t_call * 1e3, tf))
+
+    if args.calib_copy:
+        calib_copy(dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle) ...")
+        cpu = cpu_baseline(host_inputs)
+
+    line = {
+        "metric": "TP-shard MLP fwd decode weight GB/s (%HBM peak)",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode: 8 TP=8 rank shards of a 70B-class MLP (d_model 8192, "
+                               "ffn 28672, per-rank F 3584, SwiGLU, bf16) at M=32 tokens, "
+                               "computed in turn + tp_partials_reduce of the 8 fp32 partials",
+                   "global_batch": M_DECODE, "seq_len": 1, "parallelism": "tp8 shards on 1 GPU",
+                   "weight_bytes_per_step": w_bytes_step},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "down_projection": down,
+        "decode_shard": {"avg_us": round(shard_us, 2),
+                         "GBs": round(shard_bytes / (shard_us * 1e-6) / 1e9, 1),
+                         "algorithmic_bytes": shard_bytes},
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+        "device": props.name,
+        "source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
