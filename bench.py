@@ -9,12 +9,15 @@ then the down projection into an fp32 partial), and ``tp_partials_reduce`` sums 
 eight partials.  The eight shards hold 1.41 GB of distinct weights, more than the
 256 MB last-level cache, so every step streams its weights from HBM.
 
-``value`` is decode weight bandwidth: bf16 weight bytes per step / time per step.
+The step is captured once in a HIP graph and the timed region replays it back to
+back (launch-bound decode steps are run from graphs in practice; the eager step
+time is reported next to it).  ``value`` is decode weight bandwidth: bf16 weight
+bytes per step / time per step.
 The JSON line also carries
 
 * ``roofline``: the dominant kernel (the gate/up projection, 2/3 of the weight
-  bytes) timed by HIP events that the library records on the launch stream around
-  every launch in the timed region, against the 8 TB/s HBM peak;
+  bytes) timed by HIP events attached to each of its launches (the library's
+  timing hook) over the same steps launched eagerly, against the 8 TB/s HBM peak;
 * ``prefill``: one rank shard at the prefill shape (M = 8192), TFLOP/s against the
   2.5 PFLOP/s dense bf16 matrix-core peak, with its own per-kernel event timing;
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
@@ -76,16 +79,16 @@ def stored_traffic(kernel: str):
 class Rank:
     """One rank's shard handle plus the raw C arguments of its fwd call."""
 
-    def __init__(self, tpm, lib, a, b, x, max_tokens, stream_ptr):
+    def __init__(self, tpm, lib, a, b, x, max_tokens):
         import torch
         self.shard = tpm.Shard(a, b, "silu_gate", max_tokens=max_tokens)
         self.out = torch.empty((x.shape[0], D_MODEL), dtype=torch.float32, device=x.device)
         self.args = (ctypes.c_void_p(self.shard.handle), ctypes.c_void_p(x.data_ptr()),
-                     ctypes.c_int64(x.shape[0]), ctypes.c_void_p(self.out.data_ptr()), stream_ptr)
+                     ctypes.c_int64(x.shape[0]), ctypes.c_void_p(self.out.data_ptr()))
         self.lib = lib
 
-    def fwd(self):
-        rc = self.lib.tp_mlp_shard_fwd(*self.args)
+    def fwd(self, stream_ptr):
+        rc = self.lib.tp_mlp_shard_fwd(*self.args, stream_ptr)
         if rc:
             raise RuntimeError("tp_mlp_shard_fwd failed: %d" % rc)
 
@@ -109,7 +112,7 @@ class EventPool:
         return (ctypes.c_void_p * 4)(*self.raw[i:i + 4]), self.ev[i:i + 4]
 
 
-def decode_workload(tpm, lib, synth, dev, stream_ptr):
+def decode_workload(tpm, lib, synth, dev):
     import torch
     spec = synth.ModelSpec()
     log("drawing the 70B-class model shards (TP=8) ...")
@@ -118,36 +121,67 @@ def decode_workload(tpm, lib, synth, dev, stream_ptr):
     x = x_cpu.to(dev)
     ranks = []
     for a, b in zip(a_sh, b_sh):
-        ranks.append(Rank(tpm, lib, a.to(dev), b.to(dev), x, M_DECODE, stream_ptr))
+        ranks.append(Rank(tpm, lib, a.to(dev), b.to(dev), x, M_DECODE))
     torch.cuda.synchronize()
     z = torch.empty((M_DECODE, D_MODEL), dtype=torch.float32, device=dev)
     parts = (ctypes.c_void_p * TP)(*[r.out.data_ptr() for r in ranks])
     red_args = (parts, ctypes.c_int32(TP), ctypes.c_int64(M_DECODE * D_MODEL), ctypes.c_int32(0),
-                ctypes.c_void_p(z.data_ptr()), ctypes.c_int32(0), stream_ptr)
+                ctypes.c_void_p(z.data_ptr()), ctypes.c_int32(0))
     return ranks, red_args, z, (x_cpu, a_sh, b_sh)
 
 
-def run_decode(lib, ranks, red_args, steps, warmup):
+def _stream_ptr(stream=None):
     import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(int(st.cuda_stream))
 
-    def step(hooks=None):
-        for i, r in enumerate(ranks):
-            if hooks is not None:
-                arr, _ = hooks[i]
-                lib.tp_mlp_shard_set_timing_events(r.args[0], arr, 4)
-            r.fwd()
-        rc = lib.tp_partials_reduce(*red_args)
-        if rc:
-            raise RuntimeError("tp_partials_reduce failed: %d" % rc)
 
+def decode_step(lib, ranks, red_args, stream_ptr, hooks=None):
+    """One decode step: the 8 rank shards in turn, then the partials sum."""
+    for i, r in enumerate(ranks):
+        if hooks is not None:
+            lib.tp_mlp_shard_set_timing_events(r.args[0], hooks[i][0], 4)
+        r.fwd(stream_ptr)
+    rc = lib.tp_partials_reduce(*red_args, stream_ptr)
+    if rc:
+        raise RuntimeError("tp_partials_reduce failed: %d" % rc)
+
+
+def run_decode_graph(lib, ranks, red_args, steps, warmup):
+    """Capture one decode step in a HIP graph and time `steps` replays of it."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_step(lib, ranks, red_args, _stream_ptr(side))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        decode_step(lib, ranks, red_args, _stream_ptr())
     for _ in range(warmup):
-        step()
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return t1 - t0, g
+
+
+def run_decode_eager(lib, ranks, red_args, steps, warmup):
+    """`steps` eager decode steps, every kernel timed by events attached to its launch."""
+    import torch
+    sp = _stream_ptr()
+    for _ in range(warmup):
+        decode_step(lib, ranks, red_args, sp)
     pool = EventPool(4 * len(ranks) * steps)
     hooks = [[pool.take4() for _ in ranks] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(steps):
-        step(hooks[s])
+    for st in range(steps):
+        decode_step(lib, ranks, red_args, sp, hooks[st])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for r in ranks:
@@ -157,21 +191,22 @@ def run_decode(lib, ranks, red_args, steps, warmup):
     return (t1 - t0), k1, k2
 
 
-def run_prefill(tpm, lib, synth, dev, stream_ptr, iters, warmup):
+def run_prefill(tpm, lib, synth, dev, iters, warmup):
     import torch
     a, b = synth.ModelSpec().shard(0, TP)
     x = synth.tokens(M_PREFILL).to(dev)
-    r = Rank(tpm, lib, a.to(dev), b.to(dev), x, M_PREFILL, stream_ptr)
+    r = Rank(tpm, lib, a.to(dev), b.to(dev), x, M_PREFILL)
     del a, b
+    sp = _stream_ptr()
     for _ in range(warmup):
-        r.fwd()
+        r.fwd(sp)
     pool = EventPool(4 * iters)
     hooks = [pool.take4() for _ in range(iters)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for arr, _ in hooks:
         lib.tp_mlp_shard_set_timing_events(r.args[0], arr, 4)
-        r.fwd()
+        r.fwd(sp)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
@@ -252,17 +287,21 @@ def main():
     lib = tpm.capi()  # raises if libtpmlp.so is not built: there is no fallback
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream_ptr = ctypes.c_void_p(int(torch.cuda.current_stream().cuda_stream))
     props = torch.cuda.get_device_properties(dev)
     log("device:", props.name, "CUs:", props.multi_processor_count)
 
-    ranks, red_args, _, host_inputs = decode_workload(tpm, lib, synth, dev, stream_ptr)
+    ranks, red_args, _, host_inputs = decode_workload(tpm, lib, synth, dev)
     w_bytes_rank = D_MODEL * 2 * (FFN // TP) * 2 + (FFN // TP) * D_MODEL * 2
     w_bytes_step = TP * w_bytes_rank
-    log("decode: %d steps (warmup %d) ..." % (args.steps, args.warmup))
-    elapsed, k1, k2 = run_decode(lib, ranks, red_args, args.steps, args.warmup)
+    log("decode: %d steps (warmup %d), HIP-graph replay ..." % (args.steps, args.warmup))
+    elapsed, graph = run_decode_graph(lib, ranks, red_args, args.steps, args.warmup)
     ms_step = elapsed / args.steps * 1e3
     value = w_bytes_step / (elapsed / args.steps) / 1e9
+    del graph
+    log("decode: the same %d steps launched eagerly, each kernel timed by its own events ..."
+        % args.steps)
+    elapsed_eager, k1, k2 = run_decode_eager(lib, ranks, red_args, args.steps, args.warmup)
+    ms_step_eager = elapsed_eager / args.steps * 1e3
 
     F = FFN // TP
     k1_bytes = D_MODEL * 2 * F * 2 + M_DECODE * D_MODEL * 2 + M_DECODE * F * 2
@@ -276,14 +315,16 @@ def main():
                 "traffic": traffic,
                 "kernel": "k_stream<SILU_GATE> (gate/up projection, decode shard M=32)",
                 "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
-                "launches": len(k1)}
+                "launches": len(k1),
+                "timing": "HIP events attached to each launch (start/end of execution), "
+                          "eager pass of the same steps right after the timed replays"}
     down = {"kernel": "k_stream<OUT_F32> (down projection, decode shard M=32)",
             "algorithmic_bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2),
             "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)}
     shard_us = (k1_ms + k2_ms) * 1e3
     shard_bytes = w_bytes_rank + M_DECODE * D_MODEL * 2 + M_DECODE * D_MODEL * 4
-    log("decode: %.3f ms/step, %.1f GB/s weights; gate/up %.2f us, down %.2f us"
-        % (ms_step, value, k1_ms * 1e3, k2_ms * 1e3))
+    log("decode: %.3f ms/step (graph), %.3f ms/step (eager), %.1f GB/s weights; "
+        "gate/up %.2f us, down %.2f us" % (ms_step, ms_step_eager, value, k1_ms * 1e3, k2_ms * 1e3))
 
     prefill = None
     if not args.no_prefill:
@@ -292,7 +333,7 @@ def main():
         ranks = None
         torch.cuda.empty_cache()
         log("prefill: %d iterations ..." % args.prefill_iters)
-        t_call, p1, p2 = run_prefill(tpm, lib, synth, dev, stream_ptr, args.prefill_iters, 3)
+        t_call, p1, p2 = run_prefill(tpm, lib, synth, dev, args.prefill_iters, 3)
         flops1 = 2 * M_PREFILL * D_MODEL * 2 * F
         flops2 = 2 * M_PREFILL * F * D_MODEL
         p1_ms, p2_ms = sum(p1) / len(p1), sum(p2) / len(p2)
@@ -330,7 +371,10 @@ def main():
                                "ffn 28672, per-rank F 3584, SwiGLU, bf16) at M=32 tokens, "
                                "computed in turn + tp_partials_reduce of the 8 fp32 partials",
                    "global_batch": M_DECODE, "seq_len": 1, "parallelism": "tp8 shards on 1 GPU",
-                   "weight_bytes_per_step": w_bytes_step},
+                   "weight_bytes_per_step": w_bytes_step,
+                   "launch": "each step's 17 kernels captured once in a HIP graph, timed region "
+                             "= back-to-back graph replays"},
+        "ms_per_step_eager": round(ms_step_eager, 4),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": roofline,
         "down_projection": down,

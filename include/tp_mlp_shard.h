@@ -165,11 +165,13 @@ tpm_status tp_partials_reduce(const void *const *partials_dev, int32_t k, int64_
 tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
 
 /* Timing hook for profiling.  When `events` is non-NULL, every later fwd call on
- * this handle records events[2j] on its stream just before its j-th kernel launch
- * and events[2j+1] just after it, for j < kernels_per_fwd; n_events must be at least
+ * this handle attaches events[2j] and events[2j+1] to its j-th kernel launch, for
+ * j < kernels_per_fwd: they record the start and the end of that kernel's
+ * execution (they travel with the kernel's own dispatch, so no extra work is
+ * enqueued and the stream's timing is unchanged).  n_events must be at least
  * 2 * kernels_per_fwd.  The events are hipEvent_t created by the caller, passed as
  * void*, and stay owned by the caller.  events = NULL (with n_events = 0) switches
- * the hook off.  Recording events is the only thing it changes. */
+ * the hook off. */
 tpm_status tp_mlp_shard_set_timing_events(tpm_shard_t h, void *const *events, int32_t n_events);
 
 #ifdef __cplusplus

@@ -61,17 +61,23 @@ Sizes compute_sizes(const tpm_desc &d) {
     z.n2 = round_up(D, kTileN);
     z.w1_bytes = z.n1 * D * 2;
     z.w2_bytes = z.n2 * z.ffn_pad * 2;
-    z.hidden_bytes = d.max_tokens * z.ffn_pad * 2;
-    // Split-K scratch for the streaming path (only used when all tokens fit one
-    // group of 64 rows); the two projections run one after the other and share it.
-    const int ncb1 = silu ? 2 : 1;
-    const int64_t units1 = z.n1 / kFragN / ncb1, units2 = z.n2 / kFragN;
-    const StreamCfg c1 = stream_config(kStreamMaxTokens, units1, D / kFragK);
-    const StreamCfg c2 = stream_config(kStreamMaxTokens, units2, z.ffn_pad / kFragK);
-    const int64_t f1 = c1.ksplit > 1 ? units1 * c1.ksplit * 2 * ncb1 * 16 * 64 : 0;
-    const int64_t f2 = c2.ksplit > 1 ? units2 * c2.ksplit * 2 * 16 * 64 : 0;
-    z.splitk_floats = f1 > f2 ? f1 : f2;
-    z.n_counters = units1 > units2 ? units1 : units2;
+    z.hidden_bytes = round_up(d.max_tokens, kHiddenRowPad) * z.ffn_pad * 2;
+    // Streaming-path scratch: the largest need over the token counts that run on
+    // one token group (M <= 64), for both products (they run one after the other).
+    const int64_t tok[2] = {32, 64};
+    for (int i = 0; i < 2; ++i) {
+      if (d.max_tokens < tok[i] - 31) break;
+      const StreamPlan p1 = stream_plan(tok[i], z.n1 / kFragN, D / kFragK);
+      const StreamPlan p2 = stream_plan(tok[i], z.n2 / kFragN, z.ffn_pad / kFragK);
+      const int64_t f1 = p1.s > 1 ? (z.n1 / kFragN) * p1.s * p1.mt * 1024 : 0;
+      const int64_t f2 = p2.s > 1 ? (z.n2 / kFragN) * p2.s * p2.mt * 1024 : 0;
+      const int64_t c1 = p1.s > 1 ? z.n1 / kFragN / p1.c : 0;
+      const int64_t c2 = p2.s > 1 ? z.n2 / kFragN / p2.c : 0;
+      if (f1 > z.scratch_floats) z.scratch_floats = f1;
+      if (f2 > z.scratch_floats) z.scratch_floats = f2;
+      if (c1 > z.n_counters) z.n_counters = c1;
+      if (c2 > z.n_counters) z.n_counters = c2;
+    }
   } else {
     z.ffn_pad = F;
     z.n1 = silu ? 2 * F : F;
@@ -106,7 +112,7 @@ tpm_status tp_mlp_shard_plan(const tpm_desc *desc, tpm_plan_info *out) {
   const Sizes z = compute_sizes(*desc);
   tpm_plan_info info = {};
   info.packed_weight_bytes = z.w1_bytes + z.w2_bytes;
-  info.workspace_bytes = z.hidden_bytes + z.splitk_floats * 4 + z.n_counters * 4;
+  info.workspace_bytes = z.hidden_bytes + z.scratch_floats * 4 + z.n_counters * 4;
   info.ffn_padded = z.ffn_pad;
   info.stream_max_tokens = desc->in_dtype == TPM_BF16 ? kStreamMaxTokens : 0;
   info.kernels_per_fwd = 2;
@@ -131,10 +137,8 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
   h->ffn_pad = z.ffn_pad;
   h->n1 = z.n1;
   h->n2 = z.n2;
-  h->k1_blocks = d.d_model / kFragK;
-  h->k2_blocks = z.ffn_pad / kFragK;
-  h->splitk_floats = z.splitk_floats;
-  h->n_counters = z.n_counters;
+  h->ks1 = d.d_model / kFragK;
+  h->ks2 = z.ffn_pad / kFragK;
   h->n_events = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -147,7 +151,7 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
   const int64_t o_w2 = round_up(o_w1 + z.w1_bytes, kSubAlign);
   const int64_t o_hid = round_up(o_w2 + z.w2_bytes, kSubAlign);
   const int64_t o_sk = round_up(o_hid + z.hidden_bytes, kSubAlign);
-  const int64_t o_cnt = round_up(o_sk + z.splitk_floats * 4, kSubAlign);
+  const int64_t o_cnt = round_up(o_sk + z.scratch_floats * 4, kSubAlign);
   const int64_t total = round_up(o_cnt + z.n_counters * 4, kSubAlign);
   e = hipMalloc(&h->alloc_base, static_cast<size_t>(total));
   if (e != hipSuccess) {
@@ -160,19 +164,18 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
   h->w1 = base + o_w1;
   h->w2 = base + o_w2;
   h->hidden = z.hidden_bytes ? base + o_hid : nullptr;
-  h->splitk = z.splitk_floats ? reinterpret_cast<float *>(base + o_sk) : nullptr;
+  h->scratch = z.scratch_floats ? reinterpret_cast<float *>(base + o_sk) : nullptr;
   h->counters = z.n_counters ? reinterpret_cast<int *>(base + o_cnt) : nullptr;
 
   const bool silu = d.act == TPM_ACT_SILU_GATE;
   const int64_t a_cols = silu ? 2 * d.ffn_shard : d.ffn_shard;
   if (d.in_dtype == TPM_BF16) {
     e = launch_pack_bf16(A_dev, a_cols, d.d_model, a_cols, silu, d.ffn_shard, z.n1 / kFragN,
-                         h->k1_blocks, h->w1, s);
+                         h->ks1, h->w1, s);
     if (e == hipSuccess)
       e = launch_pack_bf16(B_dev, d.d_model, d.ffn_shard, d.d_model, false, d.ffn_shard,
-                           z.n2 / kFragN, h->k2_blocks, h->w2, s);
-    if (e == hipSuccess && h->counters)
-      e = hipMemsetAsync(h->counters, 0, static_cast<size_t>(z.n_counters * 4), s);
+                           z.n2 / kFragN, h->ks2, h->w2, s);
+    if (e == hipSuccess) e = launch_zero_i32(h->counters, z.n_counters, s);
   } else {
     e = hipMemcpyAsync(h->w1, A_dev, static_cast<size_t>(z.w1_bytes), hipMemcpyDeviceToDevice, s);
     if (e == hipSuccess)
@@ -204,56 +207,45 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int epi1 = first_epi(d.act);
   const int epi2 = d.out_dtype == TPM_F32 ? EPI_OUT_F32 : EPI_OUT_BF16;
-  const bool ev = h->n_events >= 4;
+  Timing t1, t2;
+  if (h->n_events >= 4) {
+    t1.start = h->events[0];
+    t1.stop = h->events[1];
+    t2.start = h->events[2];
+    t2.stop = h->events[3];
+  }
   hipError_t e = hipSuccess;
-  auto rec = [&](int i) {
-    if (ev && e == hipSuccess) e = hipEventRecord(h->events[i], s);
-  };
 
   if (d.in_dtype == TPM_F32) {
     const int64_t a_cols = d.act == TPM_ACT_SILU_GATE ? 2 * d.ffn_shard : d.ffn_shard;
-    rec(0);
-    if (e == hipSuccess)
-      e = launch_f32_gemm(epi1, static_cast<const float *>(X_dev), d.d_model, M, d.d_model,
-                          static_cast<const float *>(h->w1), a_cols, d.ffn_shard, d.ffn_shard,
-                          h->hidden, d.ffn_shard, s);
-    rec(1);
-    rec(2);
+    e = launch_f32_gemm(epi1, static_cast<const float *>(X_dev), d.d_model, M, d.d_model,
+                        static_cast<const float *>(h->w1), a_cols, d.ffn_shard, d.ffn_shard,
+                        h->hidden, d.ffn_shard, s, t1);
     if (e == hipSuccess)
       e = launch_f32_gemm(epi2, static_cast<const float *>(h->hidden), d.ffn_shard, M,
                           d.ffn_shard, static_cast<const float *>(h->w2), d.d_model, d.d_model, 0,
-                          partial_dev, d.d_model, s);
-    rec(3);
+                          partial_dev, d.d_model, s, t2);
     return from_hip(e);
   }
 
   int path = d.path;
   if (path == TPM_PATH_AUTO) path = M <= kStreamMaxTokens ? TPM_PATH_STREAM : TPM_PATH_TILED;
-  rec(0);
+  if (path == TPM_PATH_STREAM)
+    e = launch_stream_gemm(epi1, stream_plan(M, h->n1 / kFragN, h->ks1), X_dev, d.d_model, M,
+                           h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, h->scratch,
+                           h->counters, s, t1);
+  else
+    e = launch_tiled_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden, 0, 0,
+                          h->ks2, s, t1);
   if (e == hipSuccess) {
-    if (path == TPM_PATH_STREAM) {
-      const int64_t units1 = h->n1 / kFragN / (d.act == TPM_ACT_SILU_GATE ? 2 : 1);
-      const StreamCfg c1 = stream_config(M, units1, h->k1_blocks);
-      e = launch_stream_gemm(epi1, X_dev, d.d_model, M, h->k1_blocks, h->w1, c1, h->hidden,
-                             h->ffn_pad, h->ffn_pad, h->splitk, h->counters, s);
-    } else {
-      e = launch_tiled_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden,
-                            h->ffn_pad, h->ffn_pad, s);
-    }
+    if (path == TPM_PATH_STREAM)
+      e = launch_stream_gemm(epi2, stream_plan(M, h->n2 / kFragN, h->ks2), h->hidden, 0, M,
+                             h->ks2, h->w2, h->n2 / kFragN, partial_dev, d.d_model, d.d_model, 0,
+                             h->scratch, h->counters, s, t2);
+    else
+      e = launch_tiled_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
+                            d.d_model, d.d_model, 0, s, t2);
   }
-  rec(1);
-  rec(2);
-  if (e == hipSuccess) {
-    if (path == TPM_PATH_STREAM) {
-      const StreamCfg c2 = stream_config(M, h->n2 / kFragN, h->k2_blocks);
-      e = launch_stream_gemm(epi2, h->hidden, h->ffn_pad, M, h->k2_blocks, h->w2, c2, partial_dev,
-                             d.d_model, d.d_model, h->splitk, h->counters, s);
-    } else {
-      e = launch_tiled_gemm(epi2, h->hidden, h->ffn_pad, M, h->ffn_pad, h->w2, h->n2, partial_dev,
-                            d.d_model, d.d_model, s);
-    }
-  }
-  rec(3);
   return from_hip(e);
 }
 

@@ -1,6 +1,7 @@
 // Device-side helpers shared by the HIP kernels of libtpmlp (gfx950 / CDNA4 only).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ f32x16_t mfma_32x32x16(const u32x4_t a, const u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Contraction index of element i (0..7) of lane half h in k-step s (fragment order).
+__host__ __device__ __forceinline__ int kappa(int s, int h, int i) {
+  return 32 * (s >> 1) + 16 * h + 8 * (s & 1) + i;
 }
 
 // Row (within the 32x32 output tile) held in accumulator register r by lane l.

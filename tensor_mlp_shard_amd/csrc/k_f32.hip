@@ -48,10 +48,10 @@ k_f32(const float *__restrict__ A, int64_t lda, int M, int K, const float *__res
 template <int EPI>
 static hipError_t launch_f32_one(const float *A, int64_t lda, int64_t M, int64_t K, const float *B,
                                  int64_t ldb, int64_t N, int64_t up_off, void *out, int64_t ldo,
-                                 hipStream_t s) {
+                                 hipStream_t s, const Timing &t) {
   dim3 grid(static_cast<unsigned>((N + kF32Tile - 1) / kF32Tile),
             static_cast<unsigned>((M + kF32Tile - 1) / kF32Tile));
-  hipLaunchKernelGGL((k_f32<EPI>), grid, dim3(kF32Tile, kF32Tile), 0, s, A, lda,
+  hipExtLaunchKernelGGL((k_f32<EPI>), grid, dim3(kF32Tile, kF32Tile), 0, s, t.start, t.stop, 0, A, lda,
                      static_cast<int>(M), static_cast<int>(K), B, ldb, static_cast<int>(N), up_off,
                      out, ldo);
   return hipGetLastError();
@@ -59,13 +59,13 @@ static hipError_t launch_f32_one(const float *A, int64_t lda, int64_t M, int64_t
 
 hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int64_t K,
                            const float *B, int64_t ldb, int64_t N, int64_t up_off, void *out,
-                           int64_t ldo, hipStream_t s) {
+                           int64_t ldo, hipStream_t s, const Timing &t) {
   switch (epi) {
-    case EPI_SILU_GATE: return launch_f32_one<EPI_SILU_GATE>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s);
-    case EPI_TANH: return launch_f32_one<EPI_TANH>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s);
-    case EPI_IDENTITY: return launch_f32_one<EPI_IDENTITY>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s);
-    case EPI_OUT_F32: return launch_f32_one<EPI_OUT_F32>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s);
-    case EPI_OUT_BF16: return launch_f32_one<EPI_OUT_BF16>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s);
+    case EPI_SILU_GATE: return launch_f32_one<EPI_SILU_GATE>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s, t);
+    case EPI_TANH: return launch_f32_one<EPI_TANH>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s, t);
+    case EPI_IDENTITY: return launch_f32_one<EPI_IDENTITY>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s, t);
+    case EPI_OUT_F32: return launch_f32_one<EPI_OUT_F32>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s, t);
+    case EPI_OUT_BF16: return launch_f32_one<EPI_OUT_BF16>(A, lda, M, K, B, ldb, N, up_off, out, ldo, s, t);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,255 +1,377 @@
-// Weight-streaming projection for small token counts (decode).
+// Weight-streaming projections for small token counts (decode).
 //
-// At decode sizes the projection is a skinny product: a few tokens against a
-// weight that is read once, so the kernel is bound by HBM bandwidth, not by
-// arithmetic (page "7.4 推理侧并行", section 7.4.1: decode steps read all weights
-// for little compute; page "LLM 推理并行化", section 一: decode is memory-bound).
+// At decode sizes each weight element meets a few tokens, so the products are
+// bound by HBM bandwidth (page "7.4 推理侧并行", section 7.4.1: decode reads all
+// weights for little compute; page "LLM 推理并行化", section 一: decode is
+// memory-bound).  The kernel is built to keep HBM busy and to do nothing else:
 //
-// Design (gfx950):
-//  * The weight is pre-packed into 32x32x16 MFMA operand fragments, so every wave
-//    load is one 1 KiB fully coalesced 16-byte-per-lane read and is fed straight to
-//    the matrix core without touching LDS.
-//  * The tokens (<= 32 per MFMA tile) are the MFMA's A operand; they are small and
-//    re-read from L2 by every workgroup.
-//  * A workgroup owns one column unit (32 output columns, or a matching gate+up pair
-//    of 32 hidden features for SiLU-gate) and a slice of K; its waves split that
-//    slice again and their accumulators are summed in LDS in a fixed order.
-//  * When more workgroups are needed to keep HBM busy than there are column units,
-//    several workgroups share one unit along K (split-K).  Each writes its fp32 sum
-//    to scratch and bumps a counter; the last to arrive adds all slices in slice
-//    order, applies the epilogue and resets the counter.  Summation order never
-//    depends on arrival order, so results are bitwise reproducible.
-//  * The epilogue (SiLU(gate)*up, tanh, or the partial store) is fused: the
-//    first projection never writes pre-activations to memory.
+//  * One workgroup owns one 32-column block of the packed weight over the whole
+//    contraction, so no partial sums leave the workgroup: no split-K scratch, no
+//    atomics, no cross-workgroup fences, bitwise reproducible results.  A shard
+//    of width 3584 gives 224 workgroups for the gate/up product (16 SiLU-gate
+//    features per block) and 256 for the down product, one per compute unit.
+//  * Its waves split the contraction into contiguous runs of k-steps.  Each wave
+//    streams its run of the column block with 1 KiB fully coalesced loads that
+//    are fed straight to the matrix cores (the weight is pre-packed in operand
+//    order), with two batches of loads in flight.  The load addresses of a batch
+//    past the end of the run are clamped to the last k-step (an L2 hit) and the
+//    matching products are multiplied by zero, so the loop has no branch around a
+//    load and the compiler waits for exactly one batch at a time.
+//  * The token operand is small and read from L2: row-major X (the two lane
+//    halves read 64 contiguous bytes of a row per k-step pair, see the fragment
+//    order in tpm_internal.h) for the first product, the packed hidden buffer
+//    (1 KiB contiguous per wave load) for the second.
+//  * The waves' accumulators are summed in LDS in wave order, then the epilogue
+//    runs: SiLU(gate) * up, tanh or identity, written as bf16 into the packed
+//    hidden buffer, or the partial store.
 #include "device_common.h"
 #include "tpm_internal.h"
 
 namespace tpm {
 
-constexpr int kStreamWaves = 4;   // waves per workgroup
-constexpr int kStreamUnroll = 4;  // k-steps per software-pipelined load group
+// Launch shapes.  C column blocks per workgroup: every token fragment a wave loads
+// feeds C products, so the token operand costs 1/C of the weight traffic through
+// the vector caches.  NW waves per workgroup, D k-steps per load batch (two
+// batches in flight per wave), chosen so each shape stays in registers.
+template <int MT, int C>
+struct StreamShape {
+  static constexpr int waves = (MT == 1 && C == 1) ? 16 : 8;
+  static constexpr int depth = 4;  // k-steps per load batch (two pairs)
+};
 
-template <int EPI, int MT>
-__global__ void __launch_bounds__(kStreamWaves * 64)
-k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int k_blocks,
-         const u32x4_t *__restrict__ W, void *__restrict__ out, int64_t ldo, int n_store,
-         float *__restrict__ splitk, int *__restrict__ counters, int ksplit) {
-  constexpr int NCB = (EPI == EPI_SILU_GATE) ? 2 : 1;  // 32-column blocks per unit
-  constexpr int NW = kStreamWaves;
-  constexpr int U = kStreamUnroll;
-  constexpr int NREG = MT * NCB * 16;   // accumulator registers per lane
-  constexpr int UNIT_FLOATS = NREG * 64;
+template <int EPI>
+constexpr bool is_first() {
+  return EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
+}
 
-  __shared__ float red[NW][NREG][64];
+// Epilogue of one 32 x 32 output block whose fp32 sums sit in LDS `v` in MFMA
+// accumulator order (v[r][lane] = D[mfma32_row(r, lane)][lane % 32]).
+template <int EPI, int NT>
+__device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (*hb)[40], int tid,
+                                                int tile, int cb, int M, void *out, int64_t ldo,
+                                                int n_store, int ks_out) {
+  if constexpr (is_first<EPI>()) {
+    for (int e = tid; e < 1024; e += NT) {
+      const int r = e >> 6, l = e & 63, c = l & 31;
+      const int R = mfma32_row(r, l);
+      if constexpr (EPI == EPI_SILU_GATE) {
+        if (c < 16) hb[R][c] = f32_to_bf16(silu_f(v[r][l]) * v[r][l + 16]);
+      } else {
+        hb[R][c] = f32_to_bf16(act_f<EPI>(v[r][l]));
+      }
+    }
+    __syncthreads();
+    // Packed hidden buffer: 8 features of one row per 16-byte chunk.
+    constexpr int JW = (EPI == EPI_SILU_GATE) ? 16 : 32;  // features of this column block
+    const int j0 = cb * JW;
+    for (int e = tid; e < 32 * (JW / 8); e += NT) {
+      const int R = e & 31, q = e >> 5;
+      const int j = j0 + 8 * q;
+      const int s = 2 * (j >> 5) + ((j >> 3) & 1);
+      const int ln = 32 * ((j >> 4) & 1) + R;
+      const int64_t chunk = (static_cast<int64_t>(tile) * ks_out + s) * 64 + ln;
+      static_cast<u32x4_t *>(out)[chunk] = *reinterpret_cast<const u32x4_t *>(&hb[R][8 * q]);
+    }
+  } else {
+    for (int e = tid; e < 1024; e += NT) {
+      const int r = e >> 6, l = e & 63;
+      const int row = 32 * tile + mfma32_row(r, l);
+      const int col = 32 * cb + (l & 31);
+      if (row < M && col < n_store) {
+        const int64_t o = static_cast<int64_t>(row) * ldo + col;
+        if constexpr (EPI == EPI_OUT_F32) static_cast<float *>(out)[o] = v[r][l];
+        else static_cast<uint16_t *>(out)[o] = f32_to_bf16(v[r][l]);
+      }
+    }
+  }
+}
+
+// Grid: n_units * S * groups workgroups.  Workgroup (unit u, slice sl, group z)
+// owns column blocks [C u, C u + C) for token tiles [MT z, MT z + MT) over the
+// sl-th of S equal slices of the contraction; its waves split the slice again.
+// With S > 1 each workgroup leaves its sums in `scratch` and bumps the unit's
+// arrival counter; the last to arrive adds the S slices in slice order (so the
+// result does not depend on arrival order), runs the epilogue and resets the
+// counter to zero for the next call.  Nothing ever waits for another workgroup.
+template <int EPI, int MT, int C>
+__global__ void __launch_bounds__((StreamShape<MT, C>::waves * 64))
+k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
+         const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
+         int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters) {
+  constexpr bool FIRST = is_first<EPI>();
+  constexpr int NW = StreamShape<MT, C>::waves;
+  constexpr int D = StreamShape<MT, C>::depth;
+  constexpr int PB = D / 2;  // k-step pairs per batch
+  constexpr int NT = NW * 64;
+  // Row-major tokens are staged per wave through LDS: a batch is 32 PB contiguous
+  // contraction indices (64 PB bytes) of each token row, loaded 8 rows x 128 bytes
+  // per wave instruction (whole cache lines), then read back as MFMA fragments.
+  constexpr int XROW = 32 * PB + 8;  // staged row stride in bf16 (padded against bank conflicts)
+  constexpr int XWAVE = MT * 32 * XROW;
+  constexpr int XBYTES = FIRST ? NW * XWAVE * 2 : 0;
+  constexpr int RBYTES = NW * 16 * 64 * 4;
+  constexpr int SBYTES = XBYTES > RBYTES ? XBYTES : RBYTES;
+  static_assert(!FIRST || PB == 2, "token staging assumes 128-byte row segments");
+
+  __shared__ __attribute__((aligned(16))) char smem[SBYTES];  // token staging, then reduction
+  __shared__ float vsum[16][64];
+  __shared__ __attribute__((aligned(16))) uint16_t hb[32][40];  // h of one block, bf16
   __shared__ int s_last;
+  float (*red)[16][64] = reinterpret_cast<float (*)[16][64]>(smem);
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x;
-  const int ky = blockIdx.y;
-  const int z = blockIdx.z;
-  const int row0 = z * 32 * MT;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int u = blockIdx.x % n_units;
+  const int sl = (blockIdx.x / n_units) % S;
+  const int z = blockIdx.x / (n_units * S);
+  const int mt0 = z * MT;  // first 32-row token tile of this workgroup
 
-  // k-steps [sb, se) of this wave: the workgroup's slice of K, split over waves.
-  const int wg_lo = static_cast<int>(static_cast<int64_t>(k_blocks) * ky / ksplit);
-  const int wg_hi = static_cast<int>(static_cast<int64_t>(k_blocks) * (ky + 1) / ksplit);
-  const int len = wg_hi - wg_lo;
-  const int sb = wg_lo + len * wave / NW;
-  const int se = wg_lo + len * (wave + 1) / NW;
+  // Batches of this wave.  The contraction is cut into batches of PB k-step pairs
+  // (ks is a multiple of 4, so the count is exact); slice sl takes a contiguous run
+  // of batches and each wave a contiguous run of those, [wb_lo, wb_hi).  Loads for
+  // batch indices past the run re-read its last batch (valid addresses) and their
+  // products are multiplied by zero.
+  const int nbat_all = (ks >> 1) / PB;
+  const int b_lo = static_cast<int>(static_cast<int64_t>(nbat_all) * sl / S);
+  const int b_hi = static_cast<int>(static_cast<int64_t>(nbat_all) * (sl + 1) / S);
+  const int wb_lo = b_lo + (b_hi - b_lo) * wave / NW;
+  const int wb_hi = b_lo + (b_hi - b_lo) * (wave + 1) / NW;
+  const int nb = wb_hi - wb_lo;
 
-  const u32x4_t *wp[NCB];
+  const u32x4_t *wp = W + static_cast<int64_t>(u) * C * ks * 64 + lane;  // block c: + c*ks*64
+  // Token operand.  FIRST: row-major X; lane l loads 16 bytes of row 8 j + l / 8 of
+  // the batch's 128-byte segment, chunk l % 8.  Otherwise: packed H fragments.
+  const u32x4_t *ap[MT];
+  const uint16_t *xrow[MT * 4];
+  if constexpr (FIRST) {
 #pragma unroll
-  for (int c = 0; c < NCB; ++c)
-    wp[c] = W + (static_cast<int64_t>(unit * NCB + c) * k_blocks) * 64 + lane;
-  // Token rows beyond M read a valid row instead; MFMA rows are independent and
-  // those rows are never stored.
-  const u32x4_t *xp[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    int row = row0 + mt * 32 + (lane & 31);
-    row = row < M ? row : M - 1;
-    xp[mt] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda + 8 * (lane >> 5));
-  }
-
-  f32x16_t acc[MT][NCB];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int c = 0; c < NCB; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][c][r] = 0.0f;
-
-  u32x4_t b0[U][NCB], a0[U][MT], b1[U][NCB], a1[U][MT];
-  auto load = [&](u32x4_t (&bb)[U][NCB], u32x4_t (&aa)[U][MT], int s) {
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) bb[i][c] = wp[c][static_cast<int64_t>(s + i) * 64];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) aa[i][mt] = xp[mt][(s + i) * 2];
+    for (int j = 0; j < MT * 4; ++j) {
+      int row = 32 * mt0 + 8 * j + (lane >> 3);
+      row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
+      xrow[j] = A + static_cast<int64_t>(row) * lda + 8 * (lane & 7);
     }
-  };
-  auto compute = [&](const u32x4_t (&bb)[U][NCB], const u32x4_t (&aa)[U][MT]) {
+  } else {
 #pragma unroll
-    for (int i = 0; i < U; ++i)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) acc[mt][c] = mfma_32x32x16(aa[i][mt], bb[i][c], acc[mt][c]);
-  };
+    for (int m = 0; m < MT; ++m)
+      ap[m] = reinterpret_cast<const u32x4_t *>(A) + static_cast<int64_t>(mt0 + m) * ks * 64 + lane;
+  }
+  uint16_t *xs = reinterpret_cast<uint16_t *>(smem) + wave * XWAVE;
 
-  // Full groups of U k-steps, double-buffered in registers: the loads of group g+1
-  // are in flight while group g is multiplied.
-  int s = sb;
-  const int n_full = (se - sb) / U;
-  if (n_full > 0) {
-    int g = 0;
-    load(b0, a0, s);
-    while (true) {
-      if (g + 1 < n_full) load(b1, a1, s + U);
-      compute(b0, a0);
-      s += U;
-      if (++g >= n_full) break;
-      if (g + 1 < n_full) load(b0, a0, s + U);
-      compute(b1, a1);
-      s += U;
-      if (++g >= n_full) break;
+  f32x16_t acc[MT][C];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][c][r] = 0.0f;
+
+  if (nb > 0) {
+    // One batch in registers: weight fragments and the token operand (FIRST: the
+    // raw 16-byte pieces of the staged rows; otherwise fragments).
+    constexpr int NA = FIRST ? MT * 4 : D * MT;
+    u32x4_t w0[D][C], a0[NA], w1[D][C], a1[NA];
+    auto load = [&](u32x4_t (&wb)[D][C], u32x4_t (&ab)[NA], int b) {
+      const int p0 = PB * min(wb_lo + b, wb_hi - 1);  // first pair of the batch
+#pragma unroll
+      for (int i = 0; i < D; ++i)
+#pragma unroll
+        for (int c = 0; c < C; ++c) wb[i][c] = wp[(static_cast<int64_t>(c) * ks + 2 * p0 + i) * 64];
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int j = 0; j < MT * 4; ++j)
+          ab[j] = *reinterpret_cast<const u32x4_t *>(xrow[j] + 32 * p0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) ab[i * MT + m] = ap[m][static_cast<int64_t>(2 * p0 + i) * 64];
+      }
+    };
+    auto compute = [&](const u32x4_t (&wb)[D][C], const u32x4_t (&ab)[NA], int b) {
+      u32x4_t frag[D][MT];
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int j = 0; j < MT * 4; ++j)
+          *reinterpret_cast<u32x4_t *>(&xs[(8 * j + (lane >> 3)) * XROW + 8 * (lane & 7)]) = ab[j];
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            frag[i][m] = *reinterpret_cast<const u32x4_t *>(
+                &xs[(32 * m + (lane & 31)) * XROW + 32 * (i >> 1) + 16 * (lane >> 5) + 8 * (i & 1)]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < D; ++i)
+#pragma unroll
+          for (int m = 0; m < MT; ++m) frag[i][m] = ab[i * MT + m];
+      }
+      const bool valid = wb_lo + b < wb_hi;
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4_t zero = {0u, 0u, 0u, 0u};
+          const u32x4_t a = valid ? frag[i][m] : zero;
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[m][c] = mfma_32x32x16(a, wb[i][c], acc[m][c]);
+        }
+      }
+    };
+    load(w0, a0, 0);
+    // The scheduling barriers keep each batch's loads ahead of the previous batch's
+    // products, so the products wait only for their own batch.
+    for (int b = 0; b < nb; b += 2) {
+      load(w1, a1, b + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w0, a0, b);
+      __builtin_amdgcn_sched_barrier(0);
+      load(w0, a0, b + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(w1, a1, b + 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  for (; s < se; ++s) {  // remaining k-steps, one at a time
-    u32x4_t bb[NCB], aa[MT];
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) bb[c] = wp[c][static_cast<int64_t>(s) * 64];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) aa[mt] = xp[mt][s * 2];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) acc[mt][c] = mfma_32x32x16(aa[mt], bb[c], acc[mt][c]);
-  }
+  __syncthreads();  // token staging area becomes the reduction buffer
 
-  // Sum the waves' accumulators in LDS, wave 0 first.
+  // Per output block: sum the waves' accumulators in LDS (wave order), then either
+  // finish the block or park the sum in this slice's scratch slot.
+  constexpr int BLK = MT * C;  // 32 x 32 output blocks of this workgroup
+  const int64_t wg_slot = (static_cast<int64_t>(z) * n_units + u) * S;  // + sl
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+    for (int c = 0; c < C; ++c) {
+      __syncthreads();  // red / vsum / hb free again
 #pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave][(mt * NCB + c) * 16 + r][lane] = acc[mt][c][r];
+      for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[m][c][r];
+      __syncthreads();
+      for (int e = tid; e < 1024; e += NT) {
+        float a = red[0][e >> 6][e & 63];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) a += red[w][e >> 6][e & 63];
+        if (S == 1)
+          vsum[e >> 6][e & 63] = a;
+        else  // write-through store: complete at the device coherence point when counted
+          __hip_atomic_store(&scratch[((wg_slot + sl) * BLK + m * C + c) * 1024 + e], a,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (S == 1) {
+        __syncthreads();
+        stream_epilogue<EPI, NT>(vsum, hb, tid, mt0 + m, C * u + c, M, out, ldo, n_store, ks_out);
+      }
+    }
+  }
+  if (S == 1) return;
+
+  // Arrival.  Every thread waits until its write-through stores have completed,
+  // then one thread counts the workgroup in.  The scratch traffic never touches a
+  // non-coherent cache line, so no cache write-back or invalidation is needed
+  // (those would also evict the weight stream of the other workgroups on the XCD).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-
-  auto store = [&](const float (&v)[NCB], int mt, int r, int ln) {
-    const int row = row0 + mt * 32 + mfma32_row(r, ln);
-    const int col = unit * 32 + (ln & 31);
-    if (row >= M) return;
-    const int64_t o = static_cast<int64_t>(row) * ldo + col;
-    if constexpr (EPI == EPI_SILU_GATE) {
-      static_cast<uint16_t *>(out)[o] = f32_to_bf16(silu_f(v[0]) * v[NCB - 1]);
-    } else if constexpr (EPI == EPI_TANH || EPI == EPI_IDENTITY) {
-      static_cast<uint16_t *>(out)[o] = f32_to_bf16(act_f<EPI>(v[0]));
-    } else if constexpr (EPI == EPI_OUT_F32) {
-      if (col < n_store) static_cast<float *>(out)[o] = v[0];
-    } else {
-      if (col < n_store) static_cast<uint16_t *>(out)[o] = f32_to_bf16(v[0]);
-    }
-  };
-
-  constexpr int OUTS = MT * 16 * 64;  // outputs per unit (a gate/up pair counts once)
-  float *ws = splitk + (static_cast<int64_t>(z) * gridDim.x + unit) * ksplit * UNIT_FLOATS;
-  for (int e = threadIdx.x; e < OUTS; e += NW * 64) {
-    const int mt = e >> 10, r = (e >> 6) & 15, ln = e & 63;
-    float v[NCB];
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const int q = (mt * NCB + c) * 16 + r;
-      float a = red[0][q][ln];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) a += red[w][q][ln];
-      v[c] = a;
-    }
-    if (ksplit == 1) {
-      store(v, mt, r, ln);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NCB; ++c)
-        ws[static_cast<int64_t>(ky) * UNIT_FLOATS + ((mt * NCB + c) * 16 + r) * 64 + ln] = v[c];
-    }
-  }
-  if (ksplit == 1) return;
-
-  // Split-K: the last workgroup of this unit to arrive finishes it.
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    const int old = atomicAdd(&counters[z * gridDim.x + unit], 1);
-    s_last = (old == ksplit - 1);
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&counters[static_cast<int64_t>(z) * n_units + u], 1,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == S - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  for (int e = threadIdx.x; e < OUTS; e += NW * 64) {
-    const int mt = e >> 10, r = (e >> 6) & 15, ln = e & 63;
-    float v[NCB];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const int q = ((mt * NCB + c) * 16 + r) * 64 + ln;
-      float a = ws[q];
-      for (int p = 1; p < ksplit; ++p) a += ws[static_cast<int64_t>(p) * UNIT_FLOATS + q];
-      v[c] = a;
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      __syncthreads();
+      for (int e = tid; e < 1024; e += NT) {
+        float *p = scratch + (wg_slot * BLK + m * C + c) * 1024 + e;
+        // coherent loads: read at the device coherence point, never from a stale line
+        float a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 1; q < S; ++q)
+          a += __hip_atomic_load(p + static_cast<int64_t>(q) * BLK * 1024, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        vsum[e >> 6][e & 63] = a;
+      }
+      __syncthreads();
+      stream_epilogue<EPI, NT>(vsum, hb, tid, mt0 + m, C * u + c, M, out, ldo, n_store, ks_out);
     }
-    store(v, mt, r, ln);
   }
-  if (threadIdx.x == 0) atomicExch(&counters[z * gridDim.x + unit], 0);
+  if (tid == 0)
+    __hip_atomic_store(&counters[static_cast<int64_t>(z) * n_units + u], 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
-StreamCfg stream_config(int64_t M, int64_t units, int64_t k_blocks) {
-  StreamCfg c;
-  c.mt = M <= 32 ? 1 : 2;
-  c.units = static_cast<int>(units);
-  c.zgroups = static_cast<int>((M + 32 * c.mt - 1) / (32 * c.mt));
-  c.ksplit = 1;
-  if (c.zgroups == 1) {
-    const int64_t target_wgs = 512;
-    int64_t ks = (target_wgs + units - 1) / units;
-    const int64_t max_split = k_blocks / (kStreamWaves * 8);  // >= 8 k-steps per wave
-    if (ks > max_split) ks = max_split;
-    if (ks > 16) ks = 16;
-    if (ks < 1) ks = 1;
-    c.ksplit = static_cast<int>(ks);
-  }
-  return c;
-}
-
-template <int EPI, int MT>
-static hipError_t launch_one(const void *A, int64_t lda, int64_t M, int64_t k_blocks,
-                             const void *W, const StreamCfg &cfg, void *out, int64_t ldo,
-                             int64_t n_store, float *splitk, int *counters, hipStream_t s) {
-  dim3 grid(cfg.units, cfg.ksplit, cfg.zgroups);
-  hipLaunchKernelGGL((k_stream<EPI, MT>), grid, dim3(kStreamWaves * 64), 0, s,
-                     static_cast<const uint16_t *>(A), lda, static_cast<int>(M),
-                     static_cast<int>(k_blocks), static_cast<const u32x4_t *>(W), out, ldo,
-                     static_cast<int>(n_store), splitk, counters, cfg.ksplit);
+template <int EPI, int MT, int C>
+hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
+                             int64_t n_cb, int S, void *out, int64_t ldo, int64_t n_store,
+                             int64_t ks_out, float *scratch, int *counters, hipStream_t s,
+                             const Timing &t = Timing()) {
+  const int64_t groups = (M + 32 * MT - 1) / (32 * MT);
+  const int64_t n_units = n_cb / C;
+  const int64_t blocks = n_units * S * groups;
+  if (n_cb % C || S < 1 || (S > 1 && (!scratch || !counters)) || blocks > 0x7fffffff)
+    return hipErrorInvalidConfiguration;
+  hipExtLaunchKernelGGL((k_stream<EPI, MT, C>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(StreamShape<MT, C>::waves * 64), 0, s, t.start, t.stop, 0,
+                     static_cast<const uint16_t *>(A),
+                     lda, static_cast<int>(M), static_cast<int>(ks),
+                     static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
+                     static_cast<int>(n_store), static_cast<int>(ks_out), scratch, counters);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t k_blocks,
-                              const void *W, const StreamCfg &cfg, void *out, int64_t ldo,
-                              int64_t n_store, float *splitk, int *counters, hipStream_t s) {
-#define TPM_STREAM_CASE(E)                                                                       \
-  case E:                                                                                        \
-    return cfg.mt == 1 ? launch_one<E, 1>(A, lda, M, k_blocks, W, cfg, out, ldo, n_store,        \
-                                          splitk, counters, s)                                   \
-                       : launch_one<E, 2>(A, lda, M, k_blocks, W, cfg, out, ldo, n_store,        \
-                                          splitk, counters, s);
+StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
+  StreamPlan p;
+  p.mt = M <= 32 ? 1 : 2;
+  p.c = 1;
+  p.s = 1;
+  const int64_t groups = (M + 32 * p.mt - 1) / (32 * p.mt);
+  // One column block per workgroup over the whole contraction is the fastest shape
+  // whenever there are enough blocks to occupy most compute units (measured at the
+  // 70B-class decode shapes: wider groups or contraction slices only add traffic or
+  // arrival latency there).  Narrow shards instead slice the contraction so that
+  // about 256 workgroups stream the weight.
+  const int64_t wgs = n_cb * groups;
+  if (wgs >= 192) return p;
+  int64_t s = 256 / wgs;
+  const int64_t max_s = (ks / 4) / 8;  // >= 8 batches of 2 pairs per slice
+  if (s > max_s) s = max_s;
+  if (s > kStreamMaxSlices) s = kStreamMaxSlices;
+  if (s < 1) s = 1;
+  p.s = static_cast<int>(s);
+  return p;
+}
+
+template <int E>
+static hipError_t launch_epi(const StreamPlan &plan, const void *A, int64_t lda, int64_t M,
+                             int64_t ks, const void *W, int64_t n_cb, void *out, int64_t ldo,
+                             int64_t n_store, int64_t ks_out, float *scratch, int *counters,
+                             hipStream_t s, const Timing &t) {
+  if (plan.c != 1) return hipErrorInvalidConfiguration;  // wider groups are not instantiated
+  if (plan.mt == 1)
+    return launch_stream_cfg<E, 1, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
+                                      scratch, counters, s, t);
+  return launch_stream_cfg<E, 2, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
+                                    scratch, counters, s, t);
+}
+
+hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, int64_t lda,
+                              int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
+                              int64_t ldo, int64_t n_store, int64_t ks_out, float *scratch,
+                              int *counters, hipStream_t s, const Timing &t) {
   switch (epi) {
-    TPM_STREAM_CASE(EPI_SILU_GATE)
-    TPM_STREAM_CASE(EPI_TANH)
-    TPM_STREAM_CASE(EPI_IDENTITY)
-    TPM_STREAM_CASE(EPI_OUT_F32)
-    TPM_STREAM_CASE(EPI_OUT_BF16)
+    case EPI_SILU_GATE:
+      return launch_epi<EPI_SILU_GATE>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_TANH:
+      return launch_epi<EPI_TANH>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_IDENTITY:
+      return launch_epi<EPI_IDENTITY>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_OUT_F32:
+      return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_OUT_BF16:
+      return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
     default:
       return hipErrorInvalidValue;
   }
-#undef TPM_STREAM_CASE
 }
 
 }  // namespace tpm

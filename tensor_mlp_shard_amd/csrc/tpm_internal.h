@@ -18,83 +18,126 @@ enum Epi : int {
   EPI_OUT_BF16 = 4,   // partial stored as bf16
 };
 
-
-// Packed weight layout ("fragment tiles").  A logical weight W [K x N] (K rows =
-// the contraction index) is stored as 16-byte chunks indexed
-//   ((cb * nKb + kb) * 64 + lane),   cb = column block of 32, kb = k block of 16,
-// where chunk (cb, kb, lane) holds W[16*kb + 8*(lane/32) + i][32*cb + lane%32],
-// i = 0..7, as 8 bf16.  That is exactly the B operand of one 32x32x16 bf16 MFMA for
-// a wave, so one wave-wide 1 KiB load is one operand and the bytes of a column
-// block are contiguous along K.  K is zero-padded to a multiple of 64 and N to a
-// multiple of 256.
+// ---------------------------------------------------------------------------
+// Operand layout on the matrix cores ("fragment order").
 //
-// For the SiLU-gate first weight the column blocks alternate gate / up over the
-// same hidden indices: block 2p holds gate features [32p, 32p+32), block 2p+1 the
-// up features with the same indices, so one tile always owns matching pairs.
-constexpr int kFragK = 16;       // k per MFMA fragment
-constexpr int kFragN = 32;       // columns per fragment
-constexpr int kTileM = 256;      // tiled (prefill) kernel: rows per block
-constexpr int kTileN = 256;      // tiled kernel: columns per block
-constexpr int kTileK = 64;       // tiled kernel: k per LDS stage
+// Every product runs on v_mfma_f32_32x32x16_bf16: per k-step of 16, lane l of a
+// wave supplies 8 bf16 of the A operand (row l % 32) and 8 bf16 of the B operand
+// (column l % 32), for the 8 contraction indices selected by the lane half
+// h = l / 32.  The contraction may take the indices of a k-step in any order as
+// long as both operands agree, so the library fixes one order that makes row-
+// major token loads wide: within each group of 32 contraction indices,
+//
+//   k-step s (0-based), lane half h, element i (0..7)  ->  index
+//   kappa(s, h, i) = 32 * (s / 2) + 16 * h + 8 * (s % 2) + i.
+//
+// A lane thus reads the 16 consecutive indices 32*(s/2) + 16h .. +15 of its token
+// row over the two k-steps of a pair, and the two lane halves together read 64
+// contiguous bytes of the row.
+//
+// Packed weight W [K x N] (K = contraction, rows of the logical weight): 16-byte
+// chunks at index ((cb * KS + s) * 64 + lane), KS = K_pad / 16, each holding
+// W[kappa(s, lane/32, i)][column(cb, lane % 32)], i = 0..7.  One 1 KiB wave load
+// is one B operand, and a column block is contiguous along K.  K is zero-padded
+// to a multiple of 64 and the columns to a multiple of 256.
+//
+// SiLU-gate first weight: column block cb holds 16 gate columns then the 16 up
+// columns of the same hidden features [16 cb, 16 cb + 16), so one 32x32 tile
+// computes both branches of 16 features and the epilogue pairs lane c with lane
+// c + 16.  tanh / identity first weight and the second weight: column block cb is
+// columns [32 cb, 32 cb + 32).
+//
+// Packed hidden activations H [rows x F_pad] (the A operand of the second
+// product): chunks at index ((mt * KS2 + s) * 64 + lane), KS2 = F_pad / 16, each
+// holding H[32 mt + lane % 32][kappa(s, lane/32, i)], i = 0..7.  The first
+// product writes H in this order, so the second reads it with 1 KiB contiguous
+// wave loads.  Rows are padded to a multiple of 256 and every padded row holds
+// finite values.
+// ---------------------------------------------------------------------------
+constexpr int kFragK = 16;            // k per MFMA step
+constexpr int kFragN = 32;            // columns per fragment
+constexpr int kTileM = 256;           // tiled (prefill) kernel: rows per block
+constexpr int kTileN = 256;           // tiled kernel: columns per block
+constexpr int kTileK = 64;            // tiled kernel: k per LDS stage
+constexpr int kHiddenRowPad = 256;    // rows of the packed hidden buffer are padded to this
 constexpr int kStreamMaxTokens = 64;  // AUTO: streaming kernels for M <= this
+constexpr int kStreamMaxSlices = 16;  // streaming kernels: most contraction slices per block
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-struct StreamCfg {
-  int mt;      // 32-row token tiles per wave (1 or 2)
-  int ksplit;  // workgroups sharing one column unit along K
-  int units;   // column units (one or two 32-column blocks each)
-  int zgroups; // token groups of 32*mt rows (grid z)
-};
 
 struct Shard {
   tpm_desc desc;
   int device;
-  int64_t ffn_pad;   // F padded (bf16 path)
-  int64_t n1;        // packed columns of the first weight
-  int64_t n2;        // packed columns of the second weight (d padded to 256)
-  int64_t k1_blocks; // d / 16
-  int64_t k2_blocks; // ffn_pad / 16
-  void *w1;          // packed first weight (bf16) or a copy (fp32)
-  void *w2;          // packed second weight (bf16) or a copy (fp32)
-  void *hidden;      // [max_tokens x ffn_pad] bf16, or [max_tokens x F] fp32
-  float *splitk;     // split-K partial sums (stream path)
-  int *counters;     // split-K arrival counters, zero between calls
-  int64_t splitk_floats;
-  int64_t n_counters;
-  void *alloc_base;  // single device allocation holding everything above
+  int64_t ffn_pad;    // F padded (bf16 path)
+  int64_t n1;         // packed columns of the first weight
+  int64_t n2;         // packed columns of the second weight (d padded to 256)
+  int64_t ks1;        // k-steps of the first product (d / 16)
+  int64_t ks2;        // k-steps of the second product (ffn_pad / 16)
+  void *w1;           // packed first weight (bf16) or a copy (fp32)
+  void *w2;           // packed second weight (bf16) or a copy (fp32)
+  void *hidden;       // packed H (bf16 path) or [max_tokens x F] fp32
+  float *scratch;     // streaming path: per-slice partial sums
+  int *counters;      // streaming path: per-block arrival counters, zero between calls
+  void *alloc_base;   // single device allocation holding everything above
   int64_t alloc_bytes;
   hipEvent_t events[8];
   int n_events;
 };
 
 struct Sizes {
-  int64_t ffn_pad, n1, n2, w1_bytes, w2_bytes, hidden_bytes, splitk_floats, n_counters;
+  int64_t ffn_pad, n1, n2, w1_bytes, w2_bytes, hidden_bytes, scratch_floats, n_counters;
+};
+
+// Launch shape of one streaming product: token tiles per workgroup (mt), column
+// blocks per workgroup (c) and contraction slices (s).
+struct StreamPlan {
+  int mt, c, s;
+};
+
+// The streaming shape the library uses for M tokens against n_cb column blocks
+// and ks k-steps.
+StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks);
+
+// Optional timing of one launch: the events ride on the kernel's own dispatch
+// (start and end of its execution), so timing adds no work to the stream.
+struct Timing {
+  hipEvent_t start = nullptr, stop = nullptr;
 };
 
 // Sizes of the handle's buffers for a validated descriptor.
 Sizes compute_sizes(const tpm_desc &d);
 
-// Stream-path launch shape for a GEMM with `units` column units and `k_blocks` k
-// blocks at M tokens.
-StreamCfg stream_config(int64_t M, int64_t units, int64_t k_blocks);
-
 // ---- launchers (all asynchronous on `s`) ----
+
+// Repack a row-major bf16 weight into fragment order (see above).
+//   pairs = true: SiLU-gate first weight with F gate then F up columns per row.
 hipError_t launch_pack_bf16(const void *src, int64_t ld, int64_t K, int64_t ncols_src,
-                            bool pairs, int64_t F, int64_t n_cb, int64_t k_blocks, void *dst,
+                            bool pairs, int64_t F, int64_t n_cb, int64_t ks, void *dst,
                             hipStream_t s);
 
-hipError_t launch_stream_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t k_blocks,
-                              const void *W, const StreamCfg &cfg, void *out, int64_t ldo,
-                              int64_t n_store, float *splitk, int *counters, hipStream_t s);
+// Decode-path products (any M; tuned for M <= 64).
+//   First product (epi = SILU_GATE / TANH / IDENTITY): A = X row-major [M x lda],
+//   out = packed H with ks_out k-steps.  Second product (epi = OUT_*): A = packed H
+//   with ks k-steps, out = row-major partial [M x ldo], columns < n_store stored.
+//   plan.s > 1 needs scratch (n_cb * plan.s * plan.mt * 1024 floats) and
+//   n_cb / plan.c zeroed counters.
+hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, int64_t lda,
+                              int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
+                              int64_t ldo, int64_t n_store, int64_t ks_out, float *scratch,
+                              int *counters, hipStream_t s, const Timing &t = Timing());
 
+// Zero n ints (a plain kernel, so it may be captured in a graph).
+hipError_t launch_zero_i32(int *p, int64_t n, hipStream_t s);
+
+// Prefill-path products, same operand and output conventions as above.
 hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K,
                              const void *W, int64_t n_packed, void *out, int64_t ldo,
-                             int64_t n_store, hipStream_t s);
+                             int64_t n_store, int64_t ks_out, hipStream_t s,
+                             const Timing &t = Timing());
 
 hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int64_t K,
                            const float *B, int64_t ldb, int64_t N, int64_t up_offset, void *out,
-                           int64_t ldo, hipStream_t s);
+                           int64_t ldo, hipStream_t s, const Timing &t = Timing());
 
 hipError_t launch_reduce(const void *const *parts, int k, int64_t numel, int in_dtype, void *out,
                          int out_dtype, hipStream_t s);

@@ -127,6 +127,29 @@ def test_stream_and_tiled_agree_and_are_deterministic():
         assert oracle.rel_err(r1[p], ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("M", [32, 64])
+def test_stream_sliced_contraction_narrow_shard(M):
+    """A narrow shard (few column blocks, long contraction) makes the streaming path
+    slice the contraction over several workgroups and add the slices in a fixed
+    order: check it against the oracle and for bitwise repeatability."""
+    d, ffn = 8192, 2048  # per-rank F = 256 at tp=8: 16 gate/up column blocks
+    spec = synth.ModelSpec(d_model=d, ffn=ffn, pieces=8)
+    a, b = spec.shard(5, 8)
+    x = synth.tokens(M, d)
+    say("sliced stream", M, d, b.shape[0])
+    sh = tpm.Shard(a.to(DEV), b.to(DEV), "silu_gate", max_tokens=M, path="stream")
+    try:
+        xd = x.to(DEV)
+        p1 = sh.forward(xd).cpu()
+        p2 = sh.forward(xd).cpu()
+    finally:
+        sh.close()
+    assert torch.equal(p1, p2)
+    err = oracle.rel_err(p1, oracle.shard_forward(x, a, b, "silu_gate"))
+    say("err", err)
+    assert err <= TOL_BF16
+
+
 def test_m_zero_is_noop():
     spec = synth.ModelSpec(d_model=256, ffn=512, pieces=8)
     a, b = spec.shard(0, 2)
