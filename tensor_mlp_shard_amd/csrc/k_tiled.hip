@@ -28,16 +28,45 @@
 namespace tpm {
 
 constexpr int kTiledThreads = 256;
-constexpr int kStageChunks = 8 * 4 * 64;  // 16-byte chunks per operand per stage (32 KiB)
-constexpr int kGroupRows = 4;             // tile rows per launch-order group
+constexpr int kGroupRows = 4;  // tile rows per launch-order group
 
-template <int EPI>
+// LDS ring: R stages of SP k-step pairs each.  One stage holds, per k-step, the
+// 8 token fragments (32-row blocks) and the 8 weight fragments (32-column blocks)
+// of the 256 x 256 tile, 1 KiB each, in fragment order.
+template <int SP>
+struct TiledRing {
+  static constexpr int R = 4 / SP;               // stages in the ring (128 KiB)
+  static constexpr int LA = R - 1;               // stages loaded ahead of the one computed
+  static constexpr int CHUNKS = 2 * 16 * SP;     // 1 KiB chunks per stage (tokens + weight)
+  static constexpr int PER_WAVE = CHUNKS / 4;    // chunks each wave loads per stage
+};
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this
+// wave are outstanding (and does not wait on the other counters).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds + 16 l (lds is wave-uniform).  Counted by the vector-memory counter.  The
+// builtin exists only for the device; the host pass sees an empty body.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+#endif
+}
+
+template <int EPI, int SP>
 __global__ void __launch_bounds__(kTiledThreads, 1)
 k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
         void *__restrict__ out, int64_t ldo, int n_store, int ks_out) {
   constexpr bool FIRST = EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
-  __shared__ u32x4_t lds[2][2][kStageChunks];  // [stage][0 = tokens, 1 = weight]
+  using Ring = TiledRing<SP>;
+  constexpr int R = Ring::R, LA = Ring::LA, CH = Ring::CHUNKS, PW = Ring::PER_WAVE;
+  __shared__ u32x4_t lds[R][CH][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -54,44 +83,48 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   const int tm = first_m + (t % per_group) % gm;
   const int tn = (t % per_group) / gm;
 
-  // Global -> LDS mapping.  Row-major tokens (first product): chunk c (8 bf16,
-  // indices 8c..8c+7 of the 64-wide stage) of row r goes to fragment (row block
-  // r/32, k-step 2(c/4) + c%2), lane 32((c/2)%2) + r%32.  Packed hidden rows
-  // (second product) and the weight: already in fragment order.
-  const int a_r = tid >> 3;  // 0..31, row within a 32-row block
-  const int a_c = tid & 7;   // 16-byte chunk within the 64-wide k stage
-  const u32x4_t *a_src[8];
+  // Stage layout: chunk c < 16 SP is token fragment (row block (c / 2) % 8, k-step
+  // 2 (c / 16) + c % 2 of the stage); chunk 16 SP + c the weight fragment of column
+  // block (c / 2) % 8 at the same k-step.  Wave w loads chunks [PW w, PW w + PW):
+  // the direct-to-LDS load puts lane l's 16 bytes at 16 l of the chunk, so every
+  // source address is the lane's own piece of that fragment.
+  const u32x4_t *src[PW];
+  int64_t step[PW];  // source advance per stage, in 16-byte units
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if constexpr (FIRST) {
-      int row = tm * kTileM + i * 32 + a_r;
-      row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
-      a_src[i] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda) + a_c;
+  for (int q = 0; q < PW; ++q) {
+    const int c = PW * wave + q;  // wave-uniform
+    const bool tok = c < 16 * SP;
+    const int cc = tok ? c : c - 16 * SP;
+    const int blk = (cc >> 1) & 7;                 // row or column block within the tile
+    const int kstep = 2 * (cc >> 4) + (cc & 1);    // k-step within the stage
+    if (tok) {
+      if constexpr (FIRST) {
+        int row = tm * kTileM + 32 * blk + (lane & 31);
+        row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
+        // kappa(kstep, h, 0) within the stage's 32 SP indices
+        const int k0 = 32 * (kstep >> 1) + 16 * (lane >> 5) + 8 * (kstep & 1);
+        src[q] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda + k0);
+        step[q] = 4 * SP;  // 32 SP bf16
+      } else {
+        src[q] = reinterpret_cast<const u32x4_t *>(A) +
+                 ((static_cast<int64_t>(tm) * 8 + blk) * k_blocks + kstep) * 64 + lane;
+        step[q] = 2 * SP * 64;
+      }
     } else {
-      a_src[i] = reinterpret_cast<const u32x4_t *>(A) +
-                 ((static_cast<int64_t>(tm) * 8 + i) * k_blocks + (tid >> 6)) * 64 + lane;
+      src[q] = W + ((static_cast<int64_t>(tn) * 8 + blk) * k_blocks + kstep) * 64 + lane;
+      step[q] = 2 * SP * 64;
     }
   }
-  const int a_dst = FIRST ? (2 * (a_c >> 2) + (a_c & 1)) * 64 + ((a_c >> 1) & 1) * 32 + a_r : tid;
-  const u32x4_t *b_src = W + (static_cast<int64_t>(tn) * 8 * k_blocks + (tid >> 6)) * 64 + lane;
-  // weight chunk for (column block j, stage kt) = b_src + (j * k_blocks + 4 * kt) * 64
-
-  u32x4_t ra[8], rb[8];
-  auto gload = [&](int kt) {
+  // Quarter `part` (0..3) of this wave's loads of a stage.
+  auto issue_part = [&](int kt, int buf, int part) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (FIRST) ra[i] = a_src[i][kt * 8];
-      else ra[i] = a_src[i][static_cast<int64_t>(4 * kt) * 64];
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      rb[j] = b_src[(static_cast<int64_t>(j) * k_blocks + 4 * kt) * 64];
+    for (int q = part * (PW / 4); q < (part + 1) * (PW / 4); ++q)
+      load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
   };
-  auto lstore = [&](int st) {
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lds[st][0][i * 256 + a_dst] = ra[i];  // FIRST: i*4*64 + slot
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lds[st][1][j * 256 + tid] = rb[j];
+    for (int q = 0; q < PW; ++q)
+      load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
   };
 
   f32x16_t acc[4][4];
@@ -102,32 +135,91 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto compute = [&](int st) {
+  // This wave's fragments for one k-step: 4 token (rows) and 4 weight (columns).
+  auto read_k = [&](int buf, int ksi, u32x4_t (&f)[8]) {
+    const int cbase = 16 * (ksi >> 1) + (ksi & 1);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      u32x4_t fa[4], fb[4];
+    for (int i = 0; i < 4; ++i) f[i] = lds[buf][cbase + 2 * (wm * 4 + i)][lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = lds[st][0][((wm * 4 + i) * 4 + kb) * 64 + lane];
+    for (int j = 0; j < 4; ++j) f[4 + j] = lds[buf][16 * SP + cbase + 2 * (wn * 4 + j)][lane];
+  };
+  // The 4 products of token fragment row i of one k-step.
+  auto mfma_row = [&](const u32x4_t (&f)[8], int i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = lds[st][1][((wn * 4 + j) * 4 + kb) * 64 + lane];
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(f[i], f[4 + j], acc[i][j]);
+  };
+  // Fragments q, q + 1 of one k-step (0..3 token rows, 4..7 weight columns).
+  auto read_pair = [&](int buf, int ksi, u32x4_t (&f)[8], int q) {
+    const int cbase = 16 * (ksi >> 1) + (ksi & 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(fa[i], fb[j], acc[i][j]);
+    for (int r = q; r < q + 2; ++r)
+      f[r] = r < 4 ? lds[buf][cbase + 2 * (wm * 4 + r)][lane]
+                   : lds[buf][16 * SP + cbase + 2 * (wn * 4 + (r - 4))][lane];
+  };
+  // Wait until this wave's loads of the stage after `kt` have landed (the later
+  // stages' loads may stay in flight) and its LDS reads have completed, then meet
+  // the other waves: after the barrier every wave's loads of stage kt + 1 are in
+  // LDS and nobody reads the buffer of stage kt any more.
+  auto sync_stage = [&](int kt) {
+    const int later = min(R - 2, k_tiles - 2 - kt);  // stages after kt + 1 in flight
+    if constexpr (R == 4) {
+      if (later >= 2) wait_vm<2 * PW>();
+      else if (later == 1) wait_vm<PW>();
+      else wait_vm<0>();
+    } else {
+      wait_vm<0>();
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
+    // A plain hardware barrier: no fence (it would wait for every load in flight);
+    // the empty asm statements keep the compiler from moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < k_tiles; ++kt) {
-    const int st = kt & 1;
+  static_assert(SP == 1, "the stage pipeline below is written for one k-step pair per stage");
+  // Prologue: R stages in flight, the first k-step's fragments in registers.
+#pragma unroll
+  for (int st = 0; st < R; ++st)
+    if (st < k_tiles) issue(st, st);
+  u32x4_t fc[8], fn[8];  // fragments of the current and of the next k-step
+  sync_stage(-1);
+  read_k(0, 0, fc);
+  // Stage kt: read its second k-step while the first multiplies; sync (stage
+  // kt + 1 landed, buffer of stage kt free); refill that buffer with stage kt + R;
+  // read stage kt + 1's first k-step while the second multiplies.  The last
+  // stage re-reads its own buffer instead (valid, unused).
+  // (The next fragments are read between the two halves of a k-step's products:
+  // a wait on LDS reads is always a wait for all of them, so reads issued just
+  // before products that do not need them would stall those products.)
+  //
+  // Within each half the LDS reads (and after the barrier the global->LDS loads)
+  // are spread between the rows of products, so the matrix cores never wait for
+  // an instruction burst; the scheduling barriers keep that order.
+  auto stage = [&](int kt, u32x4_t (&c)[8], u32x4_t (&n)[8]) {
     const bool more = kt + 1 < k_tiles;
-    if (more) gload(kt + 1);
-    compute(st);
-    if (more) lstore(st ^ 1);
-    __syncthreads();
-  }
+    const int cb = kt % R, nb = (more ? kt + 1 : kt) % R;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mfma_row(c, i);
+      __builtin_amdgcn_sched_barrier(0);
+      read_pair(cb, 1, n, 2 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) sync_stage(kt);
+    const bool refill = kt + R < k_tiles;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (refill) issue_part(kt + R, cb, i);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_row(n, i);
+      __builtin_amdgcn_sched_barrier(0);
+      read_pair(nb, 0, c, 2 * i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int kt = 0; kt < k_tiles; ++kt) stage(kt, fc, fn);
+  __syncthreads();  // the ring is reused by the epilogue
 
   // Epilogue.
   if constexpr (FIRST) {
@@ -195,15 +287,15 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   }
 }
 
-template <int EPI>
+template <int EPI, int SP>
 static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
                                    int64_t n_packed, void *out, int64_t ldo, int64_t n_store,
                                    int64_t ks_out, hipStream_t s, const Timing &t) {
   const int ntm = static_cast<int>((M + kTileM - 1) / kTileM);
   const int ntn = static_cast<int>(n_packed / kTileN);
-  hipExtLaunchKernelGGL((k_tiled<EPI>), dim3(ntm * ntn), dim3(kTiledThreads), 0, s, t.start, t.stop, 0,
+  hipExtLaunchKernelGGL((k_tiled<EPI, SP>), dim3(ntm * ntn), dim3(kTiledThreads), 0, s, t.start, t.stop, 0,
                      static_cast<const uint16_t *>(A), lda, static_cast<int>(M),
-                     static_cast<int>(K / kTileK), static_cast<const u32x4_t *>(W),
+                     static_cast<int>(K / (32 * SP)), static_cast<const u32x4_t *>(W),
                      static_cast<int>(K / kFragK), ntm, ntn, out, ldo, static_cast<int>(n_store),
                      static_cast<int>(ks_out));
   return hipGetLastError();
@@ -214,15 +306,15 @@ hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int
                              int64_t n_store, int64_t ks_out, hipStream_t s, const Timing &t) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_SILU_GATE, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_TANH:
-      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_TANH, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_IDENTITY:
-      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_IDENTITY, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_OUT_F32:
-      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_F32, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_OUT_BF16:
-      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_BF16, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     default:
       return hipErrorInvalidValue;
   }
