@@ -4,17 +4,18 @@
 // projections are compute-bound (page "7.4 推理侧并行", section 7.4.1: prefill is a
 // large matrix multiply).  This kernel keeps the matrix cores fed from LDS:
 //
-//  * Block tile 256 x 256 (tokens x columns), K staged 64 at a time, four waves
-//    (one per SIMD), each owning a 128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 tiles
-//    with fp32 accumulators (256 per lane).
-//  * Two LDS stages of 64 KiB (A and B, 32 KiB each): the global loads of stage k+1
-//    are issued before the MFMAs of stage k and written to LDS after them, one
-//    barrier per stage.
+//  * Block tile 256 x 256 (tokens x columns).  NW waves: four (one per SIMD, each
+//    owning a 128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 tiles, 256 fp32
+//    accumulators per lane) or eight (two per SIMD, 128 x 64 sub-tiles, so one
+//    wave's waits are covered by the other's products).
+//  * Operands go from global memory straight into an LDS ring of 128 KiB
+//    (global_load_lds: no register staging), several stages ahead of use; a wave
+//    waits only for the stage it needs, then a plain barrier.
 //  * Both operands are stored in LDS in fragment order (tpm_internal.h), so each
 //    wave reads one operand with one conflict-free 1 KiB ds_read_b128 (16 B per
 //    lane, lane-contiguous).  The weight and the packed hidden buffer arrive from
-//    HBM already in that order; row-major token rows are scattered into it on the
-//    way to LDS.
+//    HBM already in that order; each lane of a row-major token load fetches its own
+//    16 bytes of the fragment.
 //  * Work tiles are renumbered so that consecutive tiles land on the same XCD
 //    (workgroup b runs on XCD b % 8), and grouped four tile rows at a time, so
 //    tiles that share operands share that XCD's L2.
@@ -27,18 +28,22 @@
 
 namespace tpm {
 
-constexpr int kTiledThreads = 256;
 constexpr int kGroupRows = 4;  // tile rows per launch-order group
 
-// LDS ring: R stages of SP k-step pairs each.  One stage holds, per k-step, the
-// 8 token fragments (32-row blocks) and the 8 weight fragments (32-column blocks)
-// of the 256 x 256 tile, 1 KiB each, in fragment order.
-template <int SP>
-struct TiledRing {
-  static constexpr int R = 4 / SP;               // stages in the ring (128 KiB)
-  static constexpr int LA = R - 1;               // stages loaded ahead of the one computed
-  static constexpr int CHUNKS = 2 * 16 * SP;     // 1 KiB chunks per stage (tokens + weight)
-  static constexpr int PER_WAVE = CHUNKS / 4;    // chunks each wave loads per stage
+// Shape of one configuration: SP k-step pairs per LDS stage, NW waves.
+//   R      stages in the LDS ring (128 KiB in total)
+//   CH     1 KiB chunks per stage: per k-step 8 token fragments (32-row blocks)
+//          and 8 weight fragments (32-column blocks) of the 256 x 256 tile
+//   PW     chunks each wave loads per stage
+//   WNB    32-column blocks per wave (its rows are always 4 blocks = 128 rows)
+template <int SP, int NW>
+struct TiledShape {
+  static constexpr int R = 4 / SP;
+  static constexpr int CH = 32 * SP;
+  static constexpr int PW = CH / NW;
+  static constexpr int WNB = 16 / NW;
+  static constexpr int NF = 4 + WNB;  // fragments per k-step per wave
+  static_assert(PW % 4 == 0 || PW == 4 || PW == 8, "loads per stage split in quarters");
 };
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of this
@@ -58,20 +63,20 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
 #endif
 }
 
-template <int EPI, int SP>
-__global__ void __launch_bounds__(kTiledThreads, 1)
+template <int EPI, int SP, int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
 k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
         void *__restrict__ out, int64_t ldo, int n_store, int ks_out) {
   constexpr bool FIRST = EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
-  using Ring = TiledRing<SP>;
-  constexpr int R = Ring::R, LA = Ring::LA, CH = Ring::CHUNKS, PW = Ring::PER_WAVE;
+  using Sh = TiledShape<SP, NW>;
+  constexpr int R = Sh::R, CH = Sh::CH, PW = Sh::PW, WNB = Sh::WNB, NF = Sh::NF;
   __shared__ u32x4_t lds[R][CH][64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
 
   // Tile renumbering: XCD-contiguous, then grouped by kGroupRows tile rows.
   const int nt = ntm * ntn;
@@ -95,8 +100,8 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
     const int c = PW * wave + q;  // wave-uniform
     const bool tok = c < 16 * SP;
     const int cc = tok ? c : c - 16 * SP;
-    const int blk = (cc >> 1) & 7;                 // row or column block within the tile
-    const int kstep = 2 * (cc >> 4) + (cc & 1);    // k-step within the stage
+    const int blk = (cc >> 1) & 7;               // row or column block within the tile
+    const int kstep = 2 * (cc >> 4) + (cc & 1);  // k-step within the stage
     if (tok) {
       if constexpr (FIRST) {
         int row = tm * kTileM + 32 * blk + (lane & 31);
@@ -127,34 +132,35 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
       load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][WNB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WNB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // This wave's fragments for one k-step: 4 token (rows) and 4 weight (columns).
-  auto read_k = [&](int buf, int ksi, u32x4_t (&f)[8]) {
+  // Fragment f of k-step ksi of a stage: f < 4 token row block wm*4 + f, else
+  // weight column block wn*WNB + f - 4.
+  auto frag = [&](int buf, int ksi, int f) -> u32x4_t {
     const int cbase = 16 * (ksi >> 1) + (ksi & 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = lds[buf][cbase + 2 * (wm * 4 + i)][lane];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f[4 + j] = lds[buf][16 * SP + cbase + 2 * (wn * 4 + j)][lane];
+    return f < 4 ? lds[buf][cbase + 2 * (wm * 4 + f)][lane]
+                 : lds[buf][16 * SP + cbase + 2 * (wn * WNB + (f - 4))][lane];
   };
-  // The 4 products of token fragment row i of one k-step.
-  auto mfma_row = [&](const u32x4_t (&f)[8], int i) {
+  auto read_k = [&](int buf, int ksi, u32x4_t (&f)[NF]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(f[i], f[4 + j], acc[i][j]);
+    for (int q = 0; q < NF; ++q) f[q] = frag(buf, ksi, q);
   };
-  // Fragments q, q + 1 of one k-step (0..3 token rows, 4..7 weight columns).
-  auto read_pair = [&](int buf, int ksi, u32x4_t (&f)[8], int q) {
-    const int cbase = 16 * (ksi >> 1) + (ksi & 1);
+  // Fragments q, q + 1 (if they exist) of one k-step.
+  auto read_pair = [&](int buf, int ksi, u32x4_t (&f)[NF], int q) {
 #pragma unroll
     for (int r = q; r < q + 2; ++r)
-      f[r] = r < 4 ? lds[buf][cbase + 2 * (wm * 4 + r)][lane]
-                   : lds[buf][16 * SP + cbase + 2 * (wn * 4 + (r - 4))][lane];
+      if (r < NF) f[r] = frag(buf, ksi, r);
+  };
+  // The products of token fragment row i of one k-step.
+  auto mfma_row = [&](const u32x4_t (&f)[NF], int i) {
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) acc[i][j] = mfma_32x32x16(f[i], f[4 + j], acc[i][j]);
   };
   // Wait until this wave's loads of the stage after `kt` have landed (the later
   // stages' loads may stay in flight) and its LDS reads have completed, then meet
@@ -177,34 +183,35 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
     asm volatile("" ::: "memory");
   };
 
-  static_assert(SP == 1, "the stage pipeline below is written for one k-step pair per stage");
   // Prologue: R stages in flight, the first k-step's fragments in registers.
 #pragma unroll
   for (int st = 0; st < R; ++st)
     if (st < k_tiles) issue(st, st);
-  u32x4_t fc[8], fn[8];  // fragments of the current and of the next k-step
+  u32x4_t fc[NF], fn[NF];  // fragments of the current and of the next k-step
   sync_stage(-1);
   read_k(0, 0, fc);
-  // Stage kt: read its second k-step while the first multiplies; sync (stage
-  // kt + 1 landed, buffer of stage kt free); refill that buffer with stage kt + R;
-  // read stage kt + 1's first k-step while the second multiplies.  The last
-  // stage re-reads its own buffer instead (valid, unused).
-  // (The next fragments are read between the two halves of a k-step's products:
-  // a wait on LDS reads is always a wait for all of them, so reads issued just
-  // before products that do not need them would stall those products.)
-  //
-  // Within each half the LDS reads (and after the barrier the global->LDS loads)
-  // are spread between the rows of products, so the matrix cores never wait for
-  // an instruction burst; the scheduling barriers keep that order.
-  auto stage = [&](int kt, u32x4_t (&c)[8], u32x4_t (&n)[8]) {
+  // Stage kt (2 SP k-steps): each k-step's products run while the next k-step's
+  // fragments are read, a fragment pair per row of products (a wait on LDS reads
+  // is always a wait for all of them, so the reads must not sit right before
+  // products that do not need them).  Before the last k-step: sync (stage kt + 1
+  // landed, buffer of stage kt free), then refill that buffer with stage kt + R,
+  // its loads spread between the rows, while stage kt + 1's first k-step is read.
+  // The last stage re-reads its own buffer instead (valid, unused).  The
+  // scheduling barriers keep this order.
+  auto stage = [&](int kt, u32x4_t (&c)[NF], u32x4_t (&n)[NF]) {
     const bool more = kt + 1 < k_tiles;
     const int cb = kt % R, nb = (more ? kt + 1 : kt) % R;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mfma_row(c, i);
-      __builtin_amdgcn_sched_barrier(0);
-      read_pair(cb, 1, n, 2 * i);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int ksi = 0; ksi + 1 < 2 * SP; ++ksi) {
+      u32x4_t (&cur)[NF] = (ksi & 1) ? n : c;
+      u32x4_t (&nxt)[NF] = (ksi & 1) ? c : n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mfma_row(cur, i);
+        __builtin_amdgcn_sched_barrier(0);
+        read_pair(cb, ksi + 1, nxt, 2 * i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (more) sync_stage(kt);
     const bool refill = kt + R < k_tiles;
@@ -223,15 +230,17 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
 
   // Epilogue.
   if constexpr (FIRST) {
-    // h of the wave's 128 rows, 64 features per pass, staged through LDS (free
+    // h of the wave's 128 rows, FP features per pass, staged through LDS (free
     // after the last barrier of the main loop), then written as 16-byte chunks
     // of the packed hidden buffer.
     constexpr int JW = (EPI == EPI_SILU_GATE) ? 16 : 32;  // features per column block
-    constexpr int BPP = 64 / JW;                          // column blocks per pass
-    constexpr int HS = 64 + 8;                            // LDS row stride (bf16)
+    constexpr int FP = NW == 4 ? 64 : 32;                 // features per pass (LDS fits)
+    constexpr int BPP = FP / JW < WNB ? FP / JW : WNB;    // column blocks per pass
+    constexpr int FPP = BPP * JW;                         // features per pass
+    constexpr int HS = FPP + 8;                           // LDS row stride (bf16)
     uint16_t *hs = reinterpret_cast<uint16_t *>(&lds[0][0][0]) + wave * (128 * HS);
 #pragma unroll
-    for (int pass = 0; pass < 4 / BPP; ++pass) {
+    for (int pass = 0; pass < WNB / BPP; ++pass) {
 #pragma unroll
       for (int jj = 0; jj < BPP; ++jj) {
         const int j = pass * BPP + jj;
@@ -239,31 +248,31 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int R = i * 32 + mfma32_row(r, lane);
+            const int R_ = i * 32 + mfma32_row(r, lane);
             const int c = lane & 31;
             const float v = acc[i][j][r];
             if constexpr (EPI == EPI_SILU_GATE) {
               const float u = __shfl_xor(v, 16);
-              if (c < 16) hs[R * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
+              if (c < 16) hs[R_ * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
             } else {
-              hs[R * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
+              hs[R_ * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
             }
           }
         }
       }
       __syncthreads();
-      const int f0 = (tn * 8 + wn * 4 + pass * BPP) * JW;  // first feature of this pass
+      const int f0 = (tn * 8 + wn * WNB + pass * BPP) * JW;  // first feature of this pass
 #pragma unroll
-      for (int q = lane; q < 128 * 8; q += 64) {
-        const int R = q & 127, qc = q >> 7;
+      for (int q = lane; q < 128 * (FPP / 8); q += 64) {
+        const int R_ = q & 127, qc = q >> 7;
         const int jf = f0 + 8 * qc;
         const int s = 2 * (jf >> 5) + ((jf >> 3) & 1);
-        const int row = tm * kTileM + wm * 128 + R;
+        const int row = tm * kTileM + wm * 128 + R_;
         const int ln = 32 * ((jf >> 4) & 1) + (row & 31);
         const int64_t chunk = (static_cast<int64_t>(row >> 5) * ks_out + s) * 64 + ln;
-        static_cast<u32x4_t *>(out)[chunk] = *reinterpret_cast<const u32x4_t *>(&hs[R * HS + 8 * qc]);
+        static_cast<u32x4_t *>(out)[chunk] = *reinterpret_cast<const u32x4_t *>(&hs[R_ * HS + 8 * qc]);
       }
-      if (pass + 1 < 4 / BPP) __syncthreads();
+      if (pass + 1 < WNB / BPP) __syncthreads();
     }
   } else {
 #pragma unroll
@@ -273,8 +282,8 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
         const int row = tm * kTileM + (wm * 4 + i) * 32 + mfma32_row(r, lane);
         if (row >= M) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = (tn * 8 + wn * 4 + j) * 32 + (lane & 31);
+        for (int j = 0; j < WNB; ++j) {
+          const int col = (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
           const int64_t o = static_cast<int64_t>(row) * ldo + col;
           if constexpr (EPI == EPI_OUT_F32) {
             if (col < n_store) static_cast<float *>(out)[o] = acc[i][j][r];
@@ -287,17 +296,22 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   }
 }
 
-template <int EPI, int SP>
+// The configuration the library launches.
+constexpr int kTiledSP = 2;
+constexpr int kTiledWaves = 8;
+
+template <int EPI, int SP = kTiledSP, int NW = kTiledWaves>
 static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
                                    int64_t n_packed, void *out, int64_t ldo, int64_t n_store,
                                    int64_t ks_out, hipStream_t s, const Timing &t) {
   const int ntm = static_cast<int>((M + kTileM - 1) / kTileM);
   const int ntn = static_cast<int>(n_packed / kTileN);
-  hipExtLaunchKernelGGL((k_tiled<EPI, SP>), dim3(ntm * ntn), dim3(kTiledThreads), 0, s, t.start, t.stop, 0,
-                     static_cast<const uint16_t *>(A), lda, static_cast<int>(M),
-                     static_cast<int>(K / (32 * SP)), static_cast<const u32x4_t *>(W),
-                     static_cast<int>(K / kFragK), ntm, ntn, out, ldo, static_cast<int>(n_store),
-                     static_cast<int>(ks_out));
+  if (K % (32 * SP)) return hipErrorInvalidValue;
+  hipExtLaunchKernelGGL((k_tiled<EPI, SP, NW>), dim3(ntm * ntn), dim3(NW * 64), 0, s, t.start,
+                        t.stop, 0, static_cast<const uint16_t *>(A), lda, static_cast<int>(M),
+                        static_cast<int>(K / (32 * SP)), static_cast<const u32x4_t *>(W),
+                        static_cast<int>(K / kFragK), ntm, ntn, out, ldo,
+                        static_cast<int>(n_store), static_cast<int>(ks_out));
   return hipGetLastError();
 }
 
@@ -306,15 +320,15 @@ hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int
                              int64_t n_store, int64_t ks_out, hipStream_t s, const Timing &t) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_tiled_one<EPI_SILU_GATE, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_TANH:
-      return launch_tiled_one<EPI_TANH, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_IDENTITY:
-      return launch_tiled_one<EPI_IDENTITY, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_OUT_F32:
-      return launch_tiled_one<EPI_OUT_F32, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     case EPI_OUT_BF16:
-      return launch_tiled_one<EPI_OUT_BF16, 1>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
     default:
       return hipErrorInvalidValue;
   }
