@@ -236,7 +236,7 @@ def cpu_baseline(host_inputs, budget_s=12.0):
         oracle.partials_sum(parts)
         t_total += time.perf_counter() - t0
         steps_done += 1
-        if t_total >= budget_s or steps_done >= 8:
+        if t_total >= budget_s or steps_done >= 40:
             break
     weight_bytes = sum(a.shape[0] * a.shape[1] * 2 + b.shape[0] * b.shape[1] * 2
                        for a, b in zip(a_sh, b_sh))
