@@ -20,6 +20,9 @@ The JSON line also carries
   timing hook) over the same steps launched eagerly, against the 8 TB/s HBM peak;
 * ``prefill``: one rank shard at the prefill shape (M = 8192), TFLOP/s against the
   2.5 PFLOP/s dense bf16 matrix-core peak, with its own per-kernel event timing;
+* ``tp_sweep``: single-rank shards at tensor-parallel degree 1, 2, 4, 8 (per-rank
+  hidden width 28672 / k) and M in {1, 8, 32, 64, 4096}, each against its roofline;
+* ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
   same decode workload.
 
@@ -216,6 +219,145 @@ def run_prefill(tpm, lib, synth, dev, iters, warmup):
     return (t1 - t0) / iters, k1, k2
 
 
+SWEEP_TP = (1, 2, 4, 8)
+SWEEP_M = (1, 8, 32, 64, 4096)
+M_ALL_SHARDS = 2048
+
+
+def _graph_of(fn):
+    """Capture fn(stream_ptr) in a HIP graph (after one eager run on a side stream)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(_stream_ptr(side))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(_stream_ptr())
+    return g
+
+
+def _time_graph(g, reps, warmup=3):
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) * 1e-3 / reps
+
+
+def _fractions(flops, nbytes, t):
+    t_roof = max(flops / (BF16_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
+    bound = "mfma" if flops / (BF16_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+    return {"bound": bound, "roofline_us": round(t_roof * 1e6, 2),
+            "frac": round(t_roof / t, 4)}
+
+
+def run_sweep(tpm, lib, dev, host_shards8, log_fn=log):
+    """Tensor-parallel degree sweep on single-rank shards of the same model, plus the
+    eight TP=8 shards and their partials sum at M = 2048.
+
+    For each degree k the k rank shards (together the whole model, 1.41 GB) are
+    created, and for each token count M one pass over them (one tp_mlp_shard_fwd per
+    rank, ranks in turn so each call streams weights the previous call did not
+    touch) is captured in a HIP graph and replayed; the time per call is the pass
+    time / k, stream-side (HIP events around the replays), both kernels and the gap
+    between them included."""
+    import torch
+    from tensor_mlp_shard_amd import synth
+    a8, b8 = host_shards8
+    F8 = FFN // TP
+    points, all_shards = [], None
+    xs = {M: synth.tokens(M).to(dev) for M in SWEEP_M + (M_ALL_SHARDS,)}
+    for k in SWEEP_TP:
+        per = TP // k
+        F = FFN // k
+        shards = []
+        for r in range(k):
+            ps = range(r * per, (r + 1) * per)
+            gate = torch.cat([a8[p][:, :F8] for p in ps], dim=1)
+            up = torch.cat([a8[p][:, F8:] for p in ps], dim=1)
+            a = torch.cat([gate, up], dim=1).contiguous().to(dev)
+            b = torch.cat([b8[p] for p in ps], dim=0).contiguous().to(dev)
+            shards.append(tpm.Shard(a, b, "silu_gate", max_tokens=max(SWEEP_M)))
+            del a, b, gate, up
+        torch.cuda.synchronize()
+        w_bytes = D_MODEL * 2 * F * 2 + F * D_MODEL * 2
+        for M in SWEEP_M:
+            x = xs[M]
+            outs = [torch.empty((M, D_MODEL), dtype=torch.float32, device=dev) for _ in range(k)]
+            args = [(ctypes.c_void_p(sh.handle), ctypes.c_void_p(x.data_ptr()), ctypes.c_int64(M),
+                     ctypes.c_void_p(o.data_ptr())) for sh, o in zip(shards, outs)]
+
+            def one_pass(sp, args=args):
+                for a_ in args:
+                    rc = lib.tp_mlp_shard_fwd(*a_, sp)
+                    if rc:
+                        raise RuntimeError("tp_mlp_shard_fwd failed: %d" % rc)
+            g = _graph_of(one_pass)
+            reps = 4 if M > 64 else max(8, 64 // k)
+            t = _time_graph(g, reps) / k
+            del g
+            flops = 6 * M * D_MODEL * F
+            nbytes = w_bytes + M * D_MODEL * 2 + M * D_MODEL * 4
+            pt = {"tp": k, "ffn_shard": F, "M": M, "us_per_call": round(t * 1e6, 2),
+                  "GBs": round(nbytes / t / 1e9, 1), "TFLOPs": round(flops / t / 1e12, 1)}
+            pt.update(_fractions(flops, nbytes, t))
+            points.append(pt)
+            log_fn("sweep: tp %d M %5d  %9.2f us/call  %7.1f GB/s  %7.1f TFLOP/s  frac %.3f (%s)"
+                   % (k, M, pt["us_per_call"], pt["GBs"], pt["TFLOPs"], pt["frac"], pt["bound"]))
+            del outs
+        if k == TP:
+            M = M_ALL_SHARDS
+            x = xs[M]
+            outs = [torch.empty((M, D_MODEL), dtype=torch.float32, device=dev) for _ in range(k)]
+            z = torch.empty((M, D_MODEL), dtype=torch.float32, device=dev)
+            args = [(ctypes.c_void_p(sh.handle), ctypes.c_void_p(x.data_ptr()), ctypes.c_int64(M),
+                     ctypes.c_void_p(o.data_ptr())) for sh, o in zip(shards, outs)]
+            parts = (ctypes.c_void_p * k)(*[o.data_ptr() for o in outs])
+            red = (parts, ctypes.c_int32(k), ctypes.c_int64(M * D_MODEL), ctypes.c_int32(0),
+                   ctypes.c_void_p(z.data_ptr()), ctypes.c_int32(0))
+
+            def step(sp, args=args, red=red):
+                for a_ in args:
+                    rc = lib.tp_mlp_shard_fwd(*a_, sp)
+                    if rc:
+                        raise RuntimeError("tp_mlp_shard_fwd failed: %d" % rc)
+                rc = lib.tp_partials_reduce(*red, sp)
+                if rc:
+                    raise RuntimeError("tp_partials_reduce failed: %d" % rc)
+            g = _graph_of(step)
+            t = _time_graph(g, 5)
+            del g
+            flops = 6 * M * D_MODEL * FFN
+            red_bytes = (k + 1) * M * D_MODEL * 4
+            nbytes = TP * (D_MODEL * 2 * F * 2 + F * D_MODEL * 2) + k * (M * D_MODEL * 6) + red_bytes
+            all_shards = {"workload": "8 TP=8 rank shards at M=2048 in turn + tp_partials_reduce "
+                                      "of the 8 fp32 partials (HIP-graph replay)",
+                          "ms_per_step": round(t * 1e3, 4),
+                          "TFLOPs": round(flops / t / 1e12, 1)}
+            all_shards.update(_fractions(flops, nbytes, t))
+            log_fn("all 8 shards + reduce at M=%d: %.3f ms/step, %.1f TFLOP/s"
+                   % (M, t * 1e3, all_shards["TFLOPs"]))
+            del outs, z
+        for sh in shards:
+            sh.close()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return {"points": points,
+            "note": "per call: one rank shard (gate/up + SiLU-gate + down into the fp32 partial) "
+                    "at per-rank ffn 28672/tp; frac = roofline time / measured time, roofline "
+                    "time = max(flops / 2.5 PFLOP/s, (weights + X + partial bytes) / 8 TB/s); "
+                    "calls replayed from a HIP graph over all tp ranks in turn"}, all_shards
+
+
 def cpu_baseline(host_inputs, budget_s=12.0):
     """The fp64 oracle on the host over whole decode steps (8 shards at M = 32 plus
     the partials sum) until about `budget_s` seconds of oracle compute have run."""
@@ -267,6 +409,8 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the tensor-parallel degree sweep and the M=2048 eight-shard step")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -354,6 +498,16 @@ def main():
                             "avg_launch_us": round(p2_ms * 1e3, 1)}}
         log("prefill: %.3f ms/call, %.1f TFLOP/s" % (t_call * 1e3, tf))
 
+    sweep = all_shards = None
+    if not args.no_sweep:
+        if ranks is not None:
+            for r in ranks:
+                r.shard.close()
+            ranks = None
+            torch.cuda.empty_cache()
+        log("tensor-parallel degree sweep ...")
+        sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
+
     if args.calib_copy:
         calib_copy(dev)
 
@@ -382,6 +536,8 @@ def main():
                          "GBs": round(shard_bytes / (shard_us * 1e-6) / 1e9, 1),
                          "algorithmic_bytes": shard_bytes},
         "prefill": prefill,
+        "tp_sweep": sweep,
+        "all_shards_m2048": all_shards,
         "cpu_baseline": cpu,
         "device": props.name,
         "source_hash": kernel_source_hash(),

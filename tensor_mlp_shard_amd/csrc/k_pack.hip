@@ -9,7 +9,7 @@
 
 namespace tpm {
 
-// src: row-major [K x ld] bf16.  dst: n_cb * ks * 64 chunks.
+// src: row-major [K x ld] bf16.  dst: ks * n_cb * 64 chunks, k-step major.
 // pairs = false: column c = 32*cb + lane%32 is source column c (zero if
 //                c >= ncols_src).
 // pairs = true:  block cb holds, for hidden features j = 16*cb + (lane%32)%16, the
@@ -23,8 +23,8 @@ k_pack_bf16(const uint16_t *__restrict__ src, int64_t ld, int64_t K, int64_t nco
   const int64_t total = n_cb * ks * 64;
   if (idx >= total) return;
   const int lane = static_cast<int>(idx & 63);
-  const int s = static_cast<int>((idx >> 6) % ks);
-  const int64_t cb = (idx >> 6) / ks;
+  const int s = static_cast<int>((idx >> 6) / n_cb);
+  const int64_t cb = (idx >> 6) % n_cb;
   const int c = lane & 31;
   int64_t col;
   bool valid;

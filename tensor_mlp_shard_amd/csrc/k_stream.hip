@@ -11,9 +11,10 @@
 //    of width 3584 gives 224 workgroups for the gate/up product (16 SiLU-gate
 //    features per block) and 256 for the down product, one per compute unit.
 //  * Its waves split the contraction into contiguous runs of k-steps.  Each wave
-//    streams its run of the column block with 1 KiB fully coalesced loads that
-//    are fed straight to the matrix cores (the weight is pre-packed in operand
-//    order), with two batches of loads in flight.  The load addresses of a batch
+//    streams its run of the column block with 1 KiB fully coalesced,
+//    non-temporal loads that are fed straight to the matrix cores (the weight is
+//    pre-packed in operand order, k-step major, so the workgroups' streams read
+//    neighbouring memory), with two batches of loads in flight.  The load addresses of a batch
 //    past the end of the run are clamped to the last k-step (an L2 hit) and the
 //    matching products are multiplied by zero, so the loop has no branch around a
 //    load and the compiler waits for exactly one batch at a time.
@@ -139,7 +140,9 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   const int wb_hi = b_lo + (b_hi - b_lo) * (wave + 1) / NW;
   const int nb = wb_hi - wb_lo;
 
-  const u32x4_t *wp = W + static_cast<int64_t>(u) * C * ks * 64 + lane;  // block c: + c*ks*64
+  // Weight fragments of block C u + c at k-step s: wp[(s * n_cb + c) * 64].
+  const int n_cb = n_units * C;
+  const u32x4_t *wp = W + static_cast<int64_t>(u) * C * 64 + lane;
   // Token operand.  FIRST: row-major X; lane l loads 16 bytes of row 8 j + l / 8 of
   // the batch's 128-byte segment, chunk l % 8.  Otherwise: packed H fragments.
   const u32x4_t *ap[MT];
@@ -176,7 +179,8 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
 #pragma unroll
       for (int i = 0; i < D; ++i)
 #pragma unroll
-        for (int c = 0; c < C; ++c) wb[i][c] = wp[(static_cast<int64_t>(c) * ks + 2 * p0 + i) * 64];
+        for (int c = 0; c < C; ++c)  // streamed once: non-temporal
+          wb[i][c] = __builtin_nontemporal_load(&wp[(static_cast<int64_t>(2 * p0 + i) * n_cb + c) * 64]);
       if constexpr (FIRST) {
 #pragma unroll
         for (int j = 0; j < MT * 4; ++j)

@@ -116,8 +116,8 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
         step[q] = 2 * SP * 64;
       }
     } else {
-      src[q] = W + ((static_cast<int64_t>(tn) * 8 + blk) * k_blocks + kstep) * 64 + lane;
-      step[q] = 2 * SP * 64;
+      src[q] = W + (static_cast<int64_t>(kstep) * ntn * 8 + tn * 8 + blk) * 64 + lane;
+      step[q] = static_cast<int64_t>(2 * SP) * ntn * 8 * 64;
     }
   }
   // Quarter `part` (0..3) of this wave's loads of a stage.
