@@ -78,6 +78,19 @@ Sizes compute_sizes(const tpm_desc &d) {
       if (c1 > z.n_counters) z.n_counters = c1;
       if (c2 > z.n_counters) z.n_counters = c2;
     }
+    // Tiled-path scratch: the fp32 sums of the contraction halves of a split last
+    // round (at most kTiledMaxSplit tiles, never more than the tiles there are).
+    const bool tiled = d.path == TPM_PATH_TILED ||
+                       (d.path == TPM_PATH_AUTO && d.max_tokens > kStreamMaxTokens);
+    if (tiled) {
+      const int64_t tm = (d.max_tokens + kTileM - 1) / kTileM;
+      int64_t tiles = tm * (z.n1 > z.n2 ? z.n1 : z.n2) / kTileN;
+      if (tiles > kTiledMaxSplit) tiles = kTiledMaxSplit;
+      const int64_t f = 2 * tiles * kTileM * kTileN;
+      if (f > z.scratch_floats) z.scratch_floats = f;
+      if (tiles > z.n_counters) z.n_counters = tiles;
+      z.split_tiles = tiles;
+    }
   } else {
     z.ffn_pad = F;
     z.n1 = silu ? 2 * F : F;
@@ -139,10 +152,13 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
   h->n2 = z.n2;
   h->ks1 = d.d_model / kFragK;
   h->ks2 = z.ffn_pad / kFragK;
+  h->split_tiles = static_cast<int>(z.split_tiles);
   h->n_events = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipGetDevice(&h->device);
+  if (e == hipSuccess)
+    e = hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->device);
   if (e != hipSuccess) {
     delete h;
     return from_hip(e);
@@ -234,9 +250,16 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
     e = launch_stream_gemm(epi1, stream_plan(M, h->n1 / kFragN, h->ks1), X_dev, d.d_model, M,
                            h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, h->scratch,
                            h->counters, s, t1);
-  else
+  TiledSplit split;
+  if (h->scratch && h->counters && h->split_tiles > 0) {
+    split.buf = h->scratch;
+    split.cnt = h->counters;
+    split.n_cu = h->n_cu;
+    split.max_tiles = h->split_tiles;
+  }
+  if (path == TPM_PATH_TILED)
     e = launch_tiled_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden, 0, 0,
-                          h->ks2, s, t1);
+                          h->ks2, split, s, t1);
   if (e == hipSuccess) {
     if (path == TPM_PATH_STREAM)
       e = launch_stream_gemm(epi2, stream_plan(M, h->n2 / kFragN, h->ks2), h->hidden, 0, M,
@@ -244,7 +267,7 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
                              h->scratch, h->counters, s, t2);
     else
       e = launch_tiled_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
-                            d.d_model, d.d_model, 0, s, t2);
+                            d.d_model, d.d_model, 0, split, s, t2);
   }
   return from_hip(e);
 }

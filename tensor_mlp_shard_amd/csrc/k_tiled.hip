@@ -19,6 +19,12 @@
 //  * Work tiles are renumbered so that consecutive tiles land on the same XCD
 //    (workgroup b runs on XCD b % 8), and grouped four tile rows at a time, so
 //    tiles that share operands share that XCD's L2.
+//  * One workgroup holds a compute unit, so tiles run in rounds of one tile per
+//    compute unit.  When the last round would leave at least half of the units
+//    idle, its tiles are split into two halves of the contraction run by two
+//    workgroups; each half parks its fp32 sums, and the second to arrive adds the
+//    other's (addition of two values is order-free, so the result does not depend
+//    on arrival order) and runs the epilogue.
 //  * The epilogue is fused: SiLU(gate) * up (each 32-column block holds 16 gate
 //    and the 16 matching up columns; lane c meets lane c + 16 by a cross-lane
 //    exchange), tanh or identity, staged through LDS and written as bf16 in the
@@ -30,15 +36,16 @@ namespace tpm {
 
 constexpr int kGroupRows = 4;  // tile rows per launch-order group
 
-// Shape of one configuration: SP k-step pairs per LDS stage, NW waves.
-//   R      stages in the LDS ring (128 KiB in total)
+// Shape of one configuration: SP k-step pairs per LDS stage, NW waves, R stages.
+//   R      stages in the LDS ring (32 SP KiB each; at most 160 KiB in total)
 //   CH     1 KiB chunks per stage: per k-step 8 token fragments (32-row blocks)
 //          and 8 weight fragments (32-column blocks) of the 256 x 256 tile
 //   PW     chunks each wave loads per stage
 //   WNB    32-column blocks per wave (its rows are always 4 blocks = 128 rows)
-template <int SP, int NW>
+template <int SP, int NW, int RING>
 struct TiledShape {
-  static constexpr int R = 4 / SP;
+  static constexpr int R = RING;
+  static_assert(R >= 2 && R * SP <= 5, "the ring must fit the 160 KiB of LDS");
   static constexpr int CH = 32 * SP;
   static constexpr int PW = CH / NW;
   static constexpr int WNB = 16 / NW;
@@ -63,13 +70,14 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
 #endif
 }
 
-template <int EPI, int SP, int NW>
+template <int EPI, int SP, int NW, int RING>
 __global__ void __launch_bounds__(NW * 64, 1)
-k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
+k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
-        void *__restrict__ out, int64_t ldo, int n_store, int ks_out) {
+        void *__restrict__ out, int64_t ldo, int n_store, int ks_out, int n_whole,
+        uint64_t *__restrict__ split_buf, int *__restrict__ split_cnt) {
   constexpr bool FIRST = EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
-  using Sh = TiledShape<SP, NW>;
+  using Sh = TiledShape<SP, NW, RING>;
   constexpr int R = Sh::R, CH = Sh::CH, PW = Sh::PW, WNB = Sh::WNB, NF = Sh::NF;
   __shared__ u32x4_t lds[R][CH][64];
 
@@ -78,10 +86,32 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / (NW / 2), wn = wave % (NW / 2);
 
-  // Tile renumbering: XCD-contiguous, then grouped by kGroupRows tile rows.
+  // Work item.  Workgroups [0, n_whole) run whole tiles [0, n_whole); the others
+  // run one contraction half (khalf) of tiles [n_whole, nt), two per tile.
   const int nt = ntm * ntn;
-  int t = blockIdx.x;
-  if ((nt & 7) == 0) t = (t & 7) * (nt >> 3) + (t >> 3);
+  const int b = blockIdx.x;
+  const bool split = b >= n_whole;
+  int t, pair = 0, khalf = 0;
+  if (!split) {
+    // XCD-contiguous renumbering of the whole tiles
+    t = b;
+    if ((n_whole & 7) == 0) t = (b & 7) * (n_whole >> 3) + (b >> 3);
+  } else {
+    const int h = b - n_whole, rem = nt - n_whole;
+    if ((rem & 7) == 0 && (n_whole & 7) == 0) {
+      // halves of one tile 8 workgroups apart: the same XCD, so the exchange of
+      // the sums usually stays in its L2
+      pair = 8 * (h >> 4) + (h & 7);
+      khalf = (h >> 3) & 1;
+    } else {
+      pair = h >> 1;
+      khalf = h & 1;
+    }
+    t = n_whole + pair;
+  }
+  const int k_lo = split && khalf ? k_total / 2 : 0;
+  const int k_tiles = split && !khalf ? k_total / 2 : k_total - k_lo;
+  // Tile coordinates: grouped by kGroupRows tile rows.
   const int per_group = kGroupRows * ntn;
   const int first_m = (t / per_group) * kGroupRows;
   const int gm = min(ntm - first_m, kGroupRows);
@@ -119,6 +149,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
       src[q] = W + (static_cast<int64_t>(kstep) * ntn * 8 + tn * 8 + blk) * 64 + lane;
       step[q] = static_cast<int64_t>(2 * SP) * ntn * 8 * 64;
     }
+    src[q] += step[q] * k_lo;  // first stage of this workgroup's contraction range
   }
   // Quarter `part` (0..3) of this wave's loads of a stage.
   auto issue_part = [&](int kt, int buf, int part) {
@@ -168,13 +199,10 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   // LDS and nobody reads the buffer of stage kt any more.
   auto sync_stage = [&](int kt) {
     const int later = min(R - 2, k_tiles - 2 - kt);  // stages after kt + 1 in flight
-    if constexpr (R == 4) {
-      if (later >= 2) wait_vm<2 * PW>();
-      else if (later == 1) wait_vm<PW>();
-      else wait_vm<0>();
-    } else {
-      wait_vm<0>();
-    }
+    if (R >= 5 && later >= 3) wait_vm<(R >= 5 ? 3 : 0) * PW>();
+    else if (R >= 4 && later >= 2) wait_vm<(R >= 4 ? 2 : 0) * PW>();
+    else if (R >= 3 && later >= 1) wait_vm<PW>();
+    else wait_vm<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) only
     // A plain hardware barrier: no fence (it would wait for every load in flight);
     // the empty asm statements keep the compiler from moving LDS accesses across it.
@@ -227,6 +255,49 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
   };
   for (int kt = 0; kt < k_tiles; ++kt) stage(kt, fc, fn);
   __syncthreads();  // the ring is reused by the epilogue
+
+  if (split) {
+    // Park this half's sums (write-through stores: complete at the device
+    // coherence point once counted), count the workgroup in; the second to
+    // arrive reads the other half's sums with coherent loads and goes on.
+    __shared__ int s_second;
+    constexpr int NV = 4 * WNB * 8;  // 64-bit pairs of sums per thread
+    uint64_t *mine = split_buf + (static_cast<int64_t>(pair) * 2 + khalf) * (NW * 64 * NV);
+    uint64_t *other = split_buf + (static_cast<int64_t>(pair) * 2 + (khalf ^ 1)) * (NW * 64 * NV);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const uint64_t v = static_cast<uint64_t>(__float_as_uint(acc[i][j][r])) |
+                             (static_cast<uint64_t>(__float_as_uint(acc[i][j][r + 1])) << 32);
+          __hip_atomic_store(&mine[((i * WNB + j) * 8 + r / 2) * (NW * 64) + tid], v,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int old = __hip_atomic_fetch_add(&split_cnt[pair], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      s_second = old == 1;
+      if (old == 1)  // both halves in: reset for the next call
+        __hip_atomic_store(&split_cnt[pair], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_second) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const uint64_t v = __hip_atomic_load(&other[((i * WNB + j) * 8 + r / 2) * (NW * 64) + tid],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          acc[i][j][r] += __uint_as_float(static_cast<uint32_t>(v));
+          acc[i][j][r + 1] += __uint_as_float(static_cast<uint32_t>(v >> 32));
+        }
+  }
 
   // Epilogue.
   if constexpr (FIRST) {
@@ -299,36 +370,53 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_tiles,
 // The configuration the library launches.
 constexpr int kTiledSP = 2;
 constexpr int kTiledWaves = 8;
+constexpr int kTiledRing = 2;
 
-template <int EPI, int SP = kTiledSP, int NW = kTiledWaves>
+int tiled_split_tiles(int64_t tiles, int n_cu, int max_tiles) {
+  if (n_cu <= 0) return 0;
+  const int64_t rem = tiles % n_cu;
+  return (rem > 0 && 2 * rem <= n_cu && rem <= max_tiles && rem <= kTiledMaxSplit)
+             ? static_cast<int>(rem)
+             : 0;
+}
+
+template <int EPI, int SP = kTiledSP, int NW = kTiledWaves, int RING = kTiledRing>
 static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
                                    int64_t n_packed, void *out, int64_t ldo, int64_t n_store,
-                                   int64_t ks_out, hipStream_t s, const Timing &t) {
+                                   int64_t ks_out, const TiledSplit &sp, hipStream_t s,
+                                   const Timing &t) {
   const int ntm = static_cast<int>((M + kTileM - 1) / kTileM);
   const int ntn = static_cast<int>(n_packed / kTileN);
   if (K % (32 * SP)) return hipErrorInvalidValue;
-  hipExtLaunchKernelGGL((k_tiled<EPI, SP, NW>), dim3(ntm * ntn), dim3(NW * 64), 0, s, t.start,
-                        t.stop, 0, static_cast<const uint16_t *>(A), lda, static_cast<int>(M),
-                        static_cast<int>(K / (32 * SP)), static_cast<const u32x4_t *>(W),
+  const int k_total = static_cast<int>(K / (32 * SP));
+  const int split = (sp.buf && sp.cnt && k_total >= 2 * RING)
+                        ? tiled_split_tiles(static_cast<int64_t>(ntm) * ntn, sp.n_cu, sp.max_tiles)
+                        : 0;
+  const int n_whole = ntm * ntn - split;
+  hipExtLaunchKernelGGL((k_tiled<EPI, SP, NW, RING>), dim3(n_whole + 2 * split), dim3(NW * 64), 0, s,
+                        t.start, t.stop, 0, static_cast<const uint16_t *>(A), lda,
+                        static_cast<int>(M), k_total, static_cast<const u32x4_t *>(W),
                         static_cast<int>(K / kFragK), ntm, ntn, out, ldo,
-                        static_cast<int>(n_store), static_cast<int>(ks_out));
+                        static_cast<int>(n_store), static_cast<int>(ks_out), n_whole,
+                        static_cast<uint64_t *>(sp.buf), sp.cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K,
                              const void *W, int64_t n_packed, void *out, int64_t ldo,
-                             int64_t n_store, int64_t ks_out, hipStream_t s, const Timing &t) {
+                             int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
+                             const Timing &t) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     case EPI_TANH:
-      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     case EPI_IDENTITY:
-      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     case EPI_OUT_F32:
-      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     case EPI_OUT_BF16:
-      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, s, t);
+      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     default:
       return hipErrorInvalidValue;
   }

@@ -81,7 +81,9 @@ struct Shard {
   void *w2;           // packed second weight (bf16) or a copy (fp32)
   void *hidden;       // packed H (bf16 path) or [max_tokens x F] fp32
   float *scratch;     // streaming path: per-slice partial sums
-  int *counters;      // streaming path: per-block arrival counters, zero between calls
+  int *counters;      // arrival counters (streaming slices, tiled halves), zero between calls
+  int n_cu;           // compute units of the device
+  int split_tiles;    // tiled path: split tiles the scratch holds
   void *alloc_base;   // single device allocation holding everything above
   int64_t alloc_bytes;
   hipEvent_t events[8];
@@ -90,6 +92,7 @@ struct Shard {
 
 struct Sizes {
   int64_t ffn_pad, n1, n2, w1_bytes, w2_bytes, hidden_bytes, scratch_floats, n_counters;
+  int64_t split_tiles;  // tiled path: room for this many split tiles in scratch / counters
 };
 
 // Launch shape of one streaming product: token tiles per workgroup (mt), column
@@ -133,10 +136,27 @@ hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, in
 // Zero n ints (a plain kernel, so it may be captured in a graph).
 hipError_t launch_zero_i32(int *p, int64_t n, hipStream_t s);
 
+// Contraction split of the tiled products' last partial round: up to
+// kTiledMaxSplit tiles, each run as two contraction halves whose fp32 sums meet
+// in `buf` (2 * 256 * 256 floats per tile) through a zeroed arrival counter in
+// `cnt` (one per tile, left at zero).  n_cu = compute units of the device.
+// buf == nullptr turns the split off.
+constexpr int kTiledMaxSplit = 128;
+struct TiledSplit {
+  void *buf = nullptr;
+  int *cnt = nullptr;
+  int n_cu = 0;
+  int max_tiles = 0;  // capacity of buf and cnt, in tiles
+};
+
+// Tiles of a tiled product (tiles in total, on n_cu compute units, room for
+// max_tiles) that run as two contraction halves.
+int tiled_split_tiles(int64_t tiles, int n_cu, int max_tiles);
+
 // Prefill-path products, same operand and output conventions as above.
 hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K,
                              const void *W, int64_t n_packed, void *out, int64_t ldo,
-                             int64_t n_store, int64_t ks_out, hipStream_t s,
+                             int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
                              const Timing &t = Timing());
 
 hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int64_t K,
