@@ -11,11 +11,12 @@
 //  * Operands go from global memory straight into an LDS ring of 128 KiB
 //    (global_load_lds: no register staging), several stages ahead of use; a wave
 //    waits only for the stage it needs, then a plain barrier.
-//  * Both operands are stored in LDS in fragment order (tpm_internal.h), so each
-//    wave reads one operand with one conflict-free 1 KiB ds_read_b128 (16 B per
-//    lane, lane-contiguous).  The weight and the packed hidden buffer arrive from
-//    HBM already in that order; each lane of a row-major token load fetches its own
-//    16 bytes of the fragment.
+//  * The weight and the packed hidden buffer arrive already in fragment order
+//    (tpm_internal.h) and are stored so, so each wave reads one operand with one
+//    conflict-free 1 KiB ds_read_b128 (16 B per lane, lane-contiguous).
+//    Row-major tokens are loaded as whole 128-byte row segments (8 cache lines per
+//    load instead of 32 partial ones) into a swizzled layout that the fragment
+//    reads gather from without bank conflicts.
 //  * Work tiles are renumbered so that consecutive tiles land on the same XCD
 //    (workgroup b runs on XCD b % 8), and grouped four tile rows at a time, so
 //    tiles that share operands share that XCD's L2.
@@ -70,6 +71,11 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
 #endif
 }
 
+// Swizzle of the row-major token stages: piece p of tile row r sits at slot
+// 8 (r % 8) + (p ^ tok_swz(r)) of its 1 KiB chunk.  The 32 rows a fragment read
+// touches land, for any 8 or 16 consecutive lanes, on distinct 16-byte bank groups.
+__device__ __forceinline__ int tok_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 template <int EPI, int SP, int NW, int RING>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
@@ -78,6 +84,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         uint64_t *__restrict__ split_buf, int *__restrict__ split_cnt) {
   constexpr bool FIRST = EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
   using Sh = TiledShape<SP, NW, RING>;
+  static_assert(!FIRST || SP == 2, "row-major token stages are 128-byte row segments");
   constexpr int R = Sh::R, CH = Sh::CH, PW = Sh::PW, WNB = Sh::WNB, NF = Sh::NF;
   __shared__ u32x4_t lds[R][CH][64];
 
@@ -119,10 +126,11 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   const int tn = (t % per_group) / gm;
 
   // Stage layout: chunk c < 16 SP is token fragment (row block (c / 2) % 8, k-step
-  // 2 (c / 16) + c % 2 of the stage); chunk 16 SP + c the weight fragment of column
+  // 2 (c / 16) + c % 2 of the stage) for the packed hidden buffer, or 8 whole token
+  // rows for row-major X (below); chunk 16 SP + c the weight fragment of column
   // block (c / 2) % 8 at the same k-step.  Wave w loads chunks [PW w, PW w + PW):
   // the direct-to-LDS load puts lane l's 16 bytes at 16 l of the chunk, so every
-  // source address is the lane's own piece of that fragment.
+  // source address is the lane's own piece of that chunk.
   const u32x4_t *src[PW];
   int64_t step[PW];  // source advance per stage, in 16-byte units
 #pragma unroll
@@ -134,11 +142,16 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
     const int kstep = 2 * (cc >> 4) + (cc & 1);  // k-step within the stage
     if (tok) {
       if constexpr (FIRST) {
-        int row = tm * kTileM + 32 * blk + (lane & 31);
+        // Row-major tokens: chunk c holds tile rows 8 c .. 8 c + 7, each as its
+        // whole 128-byte segment of the stage (8 pieces of 16 bytes), piece p of
+        // row r at slot 8 (r % 8) + (p ^ tok_swz(r)).  Every load fetches 8 whole
+        // cache lines, and the swizzle keeps the fragment reads free of bank
+        // conflicts.
+        const int r = 8 * c + (lane >> 3);
+        int row = tm * kTileM + r;
         row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
-        // kappa(kstep, h, 0) within the stage's 32 SP indices
-        const int k0 = 32 * (kstep >> 1) + 16 * (lane >> 5) + 8 * (kstep & 1);
-        src[q] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda + k0);
+        const int piece = (lane & 7) ^ tok_swz(r);
+        src[q] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda + 8 * piece);
         step[q] = 4 * SP;  // 32 SP bf16
       } else {
         src[q] = reinterpret_cast<const u32x4_t *>(A) +
@@ -173,10 +186,25 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
 
   // Fragment f of k-step ksi of a stage: f < 4 token row block wm*4 + f, else
   // weight column block wn*WNB + f - 4.
+  // Row-major token stages: the slot of this lane's row within its chunk, and the
+  // lane's piece of k-step ksi (kappa order: 32 (ksi / 2) + 16 h + 8 (ksi % 2))
+  // after the swizzle.  The swizzle depends on the row only through lane % 32.
+  const int tok_slot = 8 * (lane & 7);
+  const int tok_x = tok_swz(lane & 31);
+  auto tok_piece = [&](int ksi) { return (4 * (ksi >> 1) + 2 * (lane >> 5) + (ksi & 1)) ^ tok_x; };
+  const u32x4_t *lds_flat = &lds[0][0][0];
   auto frag = [&](int buf, int ksi, int f) -> u32x4_t {
     const int cbase = 16 * (ksi >> 1) + (ksi & 1);
-    return f < 4 ? lds[buf][cbase + 2 * (wm * 4 + f)][lane]
-                 : lds[buf][16 * SP + cbase + 2 * (wn * WNB + (f - 4))][lane];
+    if (f < 4) {
+      if constexpr (FIRST) {
+        // chunk of rows 32 (wm 4 + f) + lane % 32
+        const int chunk = 4 * (wm * 4 + f) + ((lane & 31) >> 3);
+        return lds_flat[(buf * CH + chunk) * 64 + tok_slot + tok_piece(ksi)];
+      } else {
+        return lds[buf][cbase + 2 * (wm * 4 + f)][lane];
+      }
+    }
+    return lds[buf][16 * SP + cbase + 2 * (wn * WNB + (f - 4))][lane];
   };
   auto read_k = [&](int buf, int ksi, u32x4_t (&f)[NF]) {
 #pragma unroll
