@@ -23,6 +23,8 @@ The JSON line also carries
 * ``tp_sweep``: single-rank shards at tensor-parallel degree 1, 2, 4, 8 (per-rank
   hidden width 28672 / k) and M in {1, 8, 32, 64, 4096}, each against its roofline;
 * ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
+* ``reduce_add_rmsnorm``: the partials sum fused with the residual add and RMSNorm
+  that follow it, against the same work in two launches;
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
   same decode workload.
 
@@ -358,6 +360,62 @@ def run_sweep(tpm, lib, dev, host_shards8, log_fn=log):
                     "calls replayed from a HIP graph over all tp ranks in turn"}, all_shards
 
 
+def run_reduce_norm(lib, dev, reps=200):
+    """The step after the all-reduce: the 8 fp32 rank partials summed, the residual
+    added and RMSNorm applied, in one kernel (tp_partials_reduce_add_rmsnorm), against
+    the same work as two launches (tp_partials_reduce, then the fused call with k = 1
+    on the sum).  Residual, gamma and y in bf16, eps 1e-5; HIP-graph replays."""
+    import torch
+    out = []
+    for rows in (M_DECODE, 2048):
+        g = torch.Generator().manual_seed(rows)
+        parts = [torch.randn(rows, D_MODEL, generator=g).to(dev) for _ in range(TP)]
+        res = torch.randn(rows, D_MODEL, generator=g).to(torch.bfloat16).to(dev)
+        res_out = torch.empty_like(res)
+        gamma = torch.rand(D_MODEL, generator=g).add(0.5).to(torch.bfloat16).to(dev)
+        y = torch.empty_like(res)
+        z = torch.empty(rows, D_MODEL, dtype=torch.float32, device=dev)
+        arr = (ctypes.c_void_p * TP)(*[p.data_ptr() for p in parts])
+        one = (ctypes.c_void_p * 1)(z.data_ptr())
+        vp = ctypes.c_void_p
+
+        def fused(sp):
+            rc = lib.tp_partials_reduce_add_rmsnorm(arr, TP, rows, D_MODEL, 0, vp(res.data_ptr()),
+                                                    vp(res_out.data_ptr()), 1,
+                                                    vp(gamma.data_ptr()), ctypes.c_float(1e-5),
+                                                    vp(y.data_ptr()), 1, sp)
+            if rc:
+                raise RuntimeError("tp_partials_reduce_add_rmsnorm failed: %d" % rc)
+
+        def unfused(sp):
+            rc = lib.tp_partials_reduce(arr, TP, rows * D_MODEL, 0, vp(z.data_ptr()), 0, sp)
+            rc = rc or lib.tp_partials_reduce_add_rmsnorm(one, 1, rows, D_MODEL, 0,
+                                                          vp(res.data_ptr()),
+                                                          vp(res_out.data_ptr()), 1,
+                                                          vp(gamma.data_ptr()),
+                                                          ctypes.c_float(1e-5), vp(y.data_ptr()),
+                                                          1, sp)
+            if rc:
+                raise RuntimeError("reduce / norm failed: %d" % rc)
+        n = max(10, reps if rows <= 64 else reps // 10)
+        gf, gu = _graph_of(fused), _graph_of(unfused)
+        t_f, t_u = _time_graph(gf, n), _time_graph(gu, n)
+        del gf, gu
+        nbytes = TP * rows * D_MODEL * 4 + 3 * rows * D_MODEL * 2 + D_MODEL * 2
+        out.append({"rows": rows, "k": TP, "cols": D_MODEL, "fused_us": round(t_f * 1e6, 2),
+                    "two_launch_us": round(t_u * 1e6, 2),
+                    "fused_GBs": round(nbytes / t_f / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / t_f / 1e9 / HBM_PEAK_GBS, 4),
+                    "algorithmic_bytes": nbytes})
+        log("reduce+residual+RMSNorm rows %d: fused %.2f us, two launches %.2f us, %.1f GB/s"
+            % (rows, t_f * 1e6, t_u * 1e6, nbytes / t_f / 1e9))
+        del parts, res, res_out, gamma, y, z
+    return {"points": out,
+            "note": "8 fp32 partials + bf16 residual -> bf16 residual_out and bf16 y "
+                    "(RMSNorm, eps 1e-5); two_launch = tp_partials_reduce to fp32, then the "
+                    "same fused call with k = 1; HIP-graph replays"}
+
+
 def cpu_baseline(host_inputs, budget_s=12.0):
     """The fp64 oracle on the host over whole decode steps (8 shards at M = 32 plus
     the partials sum) until about `budget_s` seconds of oracle compute have run."""
@@ -508,6 +566,11 @@ def main():
         log("tensor-parallel degree sweep ...")
         sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
 
+    reduce_norm = None
+    if not args.no_sweep:
+        log("partials sum + residual + RMSNorm ...")
+        reduce_norm = run_reduce_norm(lib, dev)
+
     if args.calib_copy:
         calib_copy(dev)
 
@@ -538,6 +601,7 @@ def main():
         "prefill": prefill,
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,
+        "reduce_add_rmsnorm": reduce_norm,
         "cpu_baseline": cpu,
         "device": props.name,
         "source_hash": kernel_source_hash(),

@@ -161,6 +161,36 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t h, const void *X_dev, int64_t M, void *p
 tpm_status tp_partials_reduce(const void *const *partials_dev, int32_t k, int64_t numel,
                               int32_t in_dtype, void *out_dev, int32_t out_dtype, void *stream);
 
+/* The partials sum fused with what follows the all-reduce of a tensor-parallel
+ * block (page "7.4 推理侧并行", section 7.4.2: fusing the residual add and RMSNorm
+ * that follow the all-reduce into one kernel saves a round trip through device
+ * memory).  For each row r of [rows x cols], in fp32:
+ *   z               = ((p_0[r] + p_1[r]) + ...) + p_{k-1}[r]    (rank order)
+ *   h               = residual[r] + z
+ *   residual_out[r] = h                                         (rounded to res_dtype)
+ *   y[r]            = h / sqrt(mean_c(h^2) + eps) * gamma       (rounded to out_dtype)
+ * RMSNorm is not defined on the pages; this is its textbook form (no mean
+ * subtraction, no bias), with the mean of squares taken over the row's cols values
+ * of the fp32 h.
+ *
+ *   partials_dev      host array of k device pointers, each [rows x cols] of in_dtype.
+ *   k                 1 <= k <= 16.
+ *   rows              >= 0 (0 is a no-op), at most 2^31 - 1.
+ *   cols              a multiple of 8, 8 <= cols <= 32768.
+ *   residual_dev      [rows x cols] of res_dtype.
+ *   residual_out_dev  [rows x cols] of res_dtype; may be residual_dev itself.
+ *   gamma_dev         [cols] of res_dtype (the RMSNorm weight).
+ *   eps               finite, >= 0.
+ *   y_dev             [rows x cols] of out_dtype.
+ * Outputs must not overlap the partials, gamma or each other (apart from the
+ * in-place residual).  Bitwise reproducible from call to call.  Asynchronous on
+ * `stream`; allocates nothing. */
+tpm_status tp_partials_reduce_add_rmsnorm(const void *const *partials_dev, int32_t k,
+                                          int64_t rows, int64_t cols, int32_t in_dtype,
+                                          const void *residual_dev, void *residual_out_dev,
+                                          int32_t res_dtype, const void *gamma_dev, float eps,
+                                          void *y_dev, int32_t out_dtype, void *stream);
+
 /* Free a handle and its device memory (waits for the device first).  NULL is OK. */
 tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
 

@@ -14,7 +14,10 @@ It follows the pages' statement of the method:
   weight is split by columns, the second by the matching rows, and the sum of the
   rank partials equals the unsplit two-layer product;
 * same page, section 1.4.3: SwiGLU applies SiLU to the gate branch and multiplies
-  by the up branch.
+  by the up branch;
+* page "7.4 推理侧并行", section 7.4.2 (kernel fusion after the all-reduce): the
+  residual add and RMSNorm that follow the sum (``reduce_add_rmsnorm``; RMSNorm in
+  its textbook form, which the pages name without defining).
 
 Activation names: ``"tanh"``, ``"silu_gate"``, ``"identity"``.  For ``silu_gate``
 a shard's first weight has ``2F`` columns: the ``F`` gate columns, then the ``F``
@@ -162,6 +165,22 @@ def unsplit_output(x, a_shards, b_shards, activation: str = "tanh") -> np.ndarra
     """The same MLP computed without splitting: one shard holding all hidden features."""
     A, B = unsplit_weights(a_shards, b_shards, activation)
     return shard_forward(x, A, B, activation)
+
+
+def reduce_add_rmsnorm(partials, residual, gamma, eps: float):
+    """The step after the all-reduce, in fp64: for each row,
+    ``h = residual + sum_i partials[i]`` (rank order) and
+    ``y = h / sqrt(mean(h^2) + eps) * gamma``.  Returns ``(h, y)``, both [rows, cols].
+    """
+    z = partials_sum(partials)
+    R = _f64(residual)
+    g = _f64(gamma)
+    if R.shape != z.shape or R.ndim != 2 or g.shape != (R.shape[1],):
+        raise ValueError("residual must match the partials, gamma must be [cols]")
+    h = R + z
+    ms = np.mean(h * h, axis=1, keepdims=True)
+    y = h / np.sqrt(ms + float(eps)) * g[None, :]
+    return h, y
 
 
 def rel_err(got, ref) -> float:

@@ -7,7 +7,8 @@ library is not built, every call raises; there is no CPU fallback.
 The functions carry the names of the C ABI (``include/tp_mlp_shard.h``):
 
 * ``tp_mlp_shard_plan``, ``tp_mlp_shard_create``, ``tp_mlp_shard_fwd``,
-  ``tp_mlp_shard_destroy``, ``tp_partials_reduce``, ``tpm_status_str``,
+  ``tp_mlp_shard_destroy``, ``tp_partials_reduce``,
+  ``tp_partials_reduce_add_rmsnorm``, ``tpm_status_str``,
   ``tp_mlp_shard_set_timing_events``;
 
 plus two conveniences: ``Shard`` (one rank's handle) and
@@ -22,7 +23,7 @@ import os
 
 __all__ = [
     "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
-    "tp_partials_reduce", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
+    "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
     "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
 ]
 
@@ -79,6 +80,9 @@ def capi():
     lib.tp_mlp_shard_fwd.restype = ctypes.c_int
     lib.tp_partials_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, i32, vp, i32, vp]
     lib.tp_partials_reduce.restype = ctypes.c_int
+    lib.tp_partials_reduce_add_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i32, vp, vp,
+                                                   i32, vp, ctypes.c_float, vp, i32, vp]
+    lib.tp_partials_reduce_add_rmsnorm.restype = ctypes.c_int
     lib.tp_mlp_shard_destroy.argtypes = [vp]
     lib.tp_mlp_shard_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
@@ -167,6 +171,38 @@ def tp_partials_reduce(partials, out, stream=None) -> None:
     _check(capi().tp_partials_reduce(arr, len(parts), numel, _dtype_code(in_dt),
                                      _dev_ptr(out, "out"), _dtype_code(out.dtype),
                                      _stream_ptr(stream)), "tp_partials_reduce")
+
+
+def tp_partials_reduce_add_rmsnorm(partials, residual, gamma, eps, y, residual_out=None,
+                                   stream=None) -> None:
+    """Partials sum + residual add + RMSNorm per row (see the C header).
+
+    partials: k tensors [rows, cols]; residual, residual_out (default: residual,
+    in place) [rows, cols]; gamma [cols] with the residual's dtype; y [rows, cols]."""
+    parts = list(partials)
+    if not parts:
+        raise ValueError("need at least one partial")
+    if residual.dim() != 2:
+        raise ValueError("residual must be [rows, cols]")
+    rows, cols = residual.shape
+    in_dt = parts[0].dtype
+    for p in parts:
+        if tuple(p.shape) != (rows, cols) or p.dtype != in_dt:
+            raise ValueError("partials must be [rows, cols] of one dtype")
+    if residual_out is None:
+        residual_out = residual
+    if tuple(residual_out.shape) != (rows, cols) or residual_out.dtype != residual.dtype:
+        raise ValueError("residual_out must match residual")
+    if tuple(gamma.shape) != (cols,) or gamma.dtype != residual.dtype:
+        raise ValueError("gamma must be [cols] with the residual's dtype")
+    if tuple(y.shape) != (rows, cols):
+        raise ValueError("y must be [rows, cols]")
+    arr = (ctypes.c_void_p * len(parts))(*[_dev_ptr(p, "partial").value for p in parts])
+    _check(capi().tp_partials_reduce_add_rmsnorm(
+        arr, len(parts), rows, cols, _dtype_code(in_dt), _dev_ptr(residual, "residual"),
+        _dev_ptr(residual_out, "residual_out"), _dtype_code(residual.dtype),
+        _dev_ptr(gamma, "gamma"), float(eps), _dev_ptr(y, "y"), _dtype_code(y.dtype),
+        _stream_ptr(stream)), "tp_partials_reduce_add_rmsnorm")
 
 
 def tp_mlp_shard_destroy(handle: int) -> None:

@@ -289,6 +289,31 @@ tpm_status tp_partials_reduce(const void *const *partials_dev, int32_t k, int64_
                                 static_cast<hipStream_t>(stream)));
 }
 
+tpm_status tp_partials_reduce_add_rmsnorm(const void *const *partials_dev, int32_t k,
+                                          int64_t rows, int64_t cols, int32_t in_dtype,
+                                          const void *residual_dev, void *residual_out_dev,
+                                          int32_t res_dtype, const void *gamma_dev, float eps,
+                                          void *y_dev, int32_t out_dtype, void *stream) {
+  if (!partials_dev || !residual_dev || !residual_out_dev || !gamma_dev || !y_dev)
+    return TPM_ERR_INVALID_ARG;
+  for (int32_t t : {in_dtype, res_dtype, out_dtype})
+    if (t != TPM_F32 && t != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return TPM_ERR_INVALID_ARG;  // rejects NaN and inf
+  if (k < 1 || k > kMaxParts || rows < 0 || rows > 0x7fffffff) return TPM_ERR_SHAPE;
+  if (cols < 8 || cols % 8 || cols > kNormMaxCols) return TPM_ERR_SHAPE;
+  for (int i = 0; i < k; ++i) {
+    if (!partials_dev[i]) return TPM_ERR_INVALID_ARG;
+    if (!aligned(partials_dev[i])) return TPM_ERR_ALIGN;
+  }
+  if (!aligned(residual_dev) || !aligned(residual_out_dev) || !aligned(gamma_dev) ||
+      !aligned(y_dev))
+    return TPM_ERR_ALIGN;
+  if (rows == 0) return TPM_OK;
+  return from_hip(launch_reduce_norm(partials_dev, k, rows, cols, in_dtype, residual_dev,
+                                     residual_out_dev, res_dtype, gamma_dev, eps, y_dev,
+                                     out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 tpm_status tp_mlp_shard_destroy(tpm_shard_t handle) {
   Shard *h = reinterpret_cast<Shard *>(handle);
   if (!h) return TPM_OK;

@@ -59,6 +59,31 @@ __device__ __forceinline__ float load1(const void *p, int64_t e) {
   else return bf16_to_f32(static_cast<const uint16_t *>(p)[e]);
 }
 
+// acc = ((p_0 + p_1) + ...) + p_{k-1} for one chunk of 8 elements.  The loads of up
+// to 8 partials are issued together (k is uniform, so the guards are scalar
+// branches), so a chunk costs one memory round trip per 8 partials instead of one
+// per partial.
+template <int IN>
+__device__ __forceinline__ void sum_parts8(const PartPtrs &pp, int k, int64_t c, float (&acc)[8]) {
+  for (int i0 = 0; i0 < k; i0 += 8) {
+    float t[8][8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (i0 + q < k) load8<IN>(pp.p[i0 + q], c, t[q]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (i0 + q >= k) break;
+      if (i0 + q == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = t[0][j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += t[q][j];
+      }
+    }
+  }
+}
+
 template <int IN, int OUT>
 __global__ void __launch_bounds__(256)
 k_reduce(PartPtrs pp, int k, int64_t numel, void *__restrict__ out) {
@@ -67,13 +92,7 @@ k_reduce(PartPtrs pp, int k, int64_t numel, void *__restrict__ out) {
   const int64_t n8 = numel >> 3;
   for (int64_t c = gid; c < n8; c += gstride) {
     float acc[8];
-    load8<IN>(pp.p[0], c, acc);
-    for (int i = 1; i < k; ++i) {
-      float t[8];
-      load8<IN>(pp.p[i], c, t);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += t[j];
-    }
+    sum_parts8<IN>(pp, k, c, acc);
     store8<OUT>(out, c, acc);
   }
   const int64_t e = (n8 << 3) + gid;
@@ -104,6 +123,121 @@ hipError_t launch_reduce(const void *const *parts, int k, int64_t numel, int in_
   else
     hipLaunchKernelGGL((k_reduce<TPM_BF16, TPM_BF16>), grid, block, 0, s, pp, k, numel, out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// The step after the all-reduce, fused with it (page "7.4 推理侧并行", section
+// 7.4.2, the kernel-fusion remedy: the residual add and RMSNorm that follow the
+// all-reduce run in the same kernel, saving a round trip through device memory).
+// Per row: z = sum of the k partials (rank order, fp32), h = residual + z,
+// residual_out = h, y = h / sqrt(mean(h^2) + eps) * gamma.  RMSNorm is not defined
+// on the pages; this is its textbook form, computed from the fp32 h.
+//
+// One workgroup per row: each thread owns NCH chunks of 8 columns, keeps their h in
+// registers between the two passes, and the row's sum of squares meets in LDS in
+// a fixed order, so results are bitwise reproducible.  HBM-bound: the partials and
+// the residual are read once, both outputs written once.
+template <int IN, int RES, int OUT, int NCH>
+__global__ void __launch_bounds__(1024)
+k_reduce_norm(PartPtrs pp, int k, int cols8, const void *__restrict__ res_in,
+              void *__restrict__ res_out, const void *__restrict__ gamma, float eps, float inv_cols,
+              void *__restrict__ y) {
+  __shared__ float wsum[16];
+  const int tid = threadIdx.x;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * cols8;  // first chunk of the row
+  // gamma is loaded with the inputs when one chunk per thread leaves the registers
+  // for it (the common case, cols <= 8192), else after the row reduction
+  constexpr bool kEarlyGamma = NCH == 1;
+  float h[NCH][8], g[NCH][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + j * blockDim.x;
+    if (c < cols8) {
+      float r[8];
+      if constexpr (kEarlyGamma) load8<RES>(gamma, c, g[j]);
+      load8<RES>(res_in, row0 + c, r);
+      sum_parts8<IN>(pp, k, row0 + c, h[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        h[j][e] = r[e] + h[j][e];
+        ss += h[j][e] * h[j][e];
+      }
+      store8<RES>(res_out, row0 + c, h[j]);
+    }
+  }
+  // Row sum of squares: wave reduction, then the waves in order.
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float t = wsum[0];
+    for (int w = 1; w < static_cast<int>(blockDim.x >> 6); ++w) t += wsum[w];
+    wsum[0] = t;
+  }
+  __syncthreads();
+  const float inv = 1.0f / sqrtf(wsum[0] * inv_cols + eps);
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + j * blockDim.x;
+    if (c < cols8) {
+      float o[8];
+      if constexpr (!kEarlyGamma) load8<RES>(gamma, c, g[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = h[j][e] * inv * g[j][e];
+      store8<OUT>(y, row0 + c, o);
+    }
+  }
+}
+
+template <int IN, int RES, int OUT>
+static hipError_t launch_norm3(const PartPtrs &pp, int k, int64_t rows, int cols8,
+                               const void *res_in, void *res_out, const void *gamma, float eps,
+                               void *y, hipStream_t s) {
+  const int bs = cols8 >= 1024 ? 1024 : ((cols8 + 63) / 64) * 64;
+  const int nch = (cols8 + bs - 1) / bs;
+  const float inv_cols = 1.0f / static_cast<float>(8 * cols8);
+  dim3 grid(static_cast<unsigned>(rows)), block(bs);
+  if (nch == 1)
+    hipLaunchKernelGGL((k_reduce_norm<IN, RES, OUT, 1>), grid, block, 0, s, pp, k, cols8, res_in,
+                       res_out, gamma, eps, inv_cols, y);
+  else if (nch == 2)
+    hipLaunchKernelGGL((k_reduce_norm<IN, RES, OUT, 2>), grid, block, 0, s, pp, k, cols8, res_in,
+                       res_out, gamma, eps, inv_cols, y);
+  else if (nch <= 4)
+    hipLaunchKernelGGL((k_reduce_norm<IN, RES, OUT, 4>), grid, block, 0, s, pp, k, cols8, res_in,
+                       res_out, gamma, eps, inv_cols, y);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <int IN, int RES>
+static hipError_t launch_norm2(const PartPtrs &pp, int k, int64_t rows, int cols8,
+                               const void *res_in, void *res_out, const void *gamma, float eps,
+                               void *y, int out_dtype, hipStream_t s) {
+  return out_dtype == TPM_F32
+             ? launch_norm3<IN, RES, TPM_F32>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, s)
+             : launch_norm3<IN, RES, TPM_BF16>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, s);
+}
+
+hipError_t launch_reduce_norm(const void *const *parts, int k, int64_t rows, int64_t cols,
+                              int in_dtype, const void *res_in, void *res_out, int res_dtype,
+                              const void *gamma, float eps, void *y, int out_dtype,
+                              hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (cols % 8 || cols > kNormMaxCols) return hipErrorInvalidValue;
+  PartPtrs pp = {};
+  for (int i = 0; i < k; ++i) pp.p[i] = parts[i];
+  const int cols8 = static_cast<int>(cols / 8);
+  if (in_dtype == TPM_F32)
+    return res_dtype == TPM_F32
+               ? launch_norm2<TPM_F32, TPM_F32>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, out_dtype, s)
+               : launch_norm2<TPM_F32, TPM_BF16>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, out_dtype, s);
+  return res_dtype == TPM_F32
+             ? launch_norm2<TPM_BF16, TPM_F32>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, out_dtype, s)
+             : launch_norm2<TPM_BF16, TPM_BF16>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, out_dtype, s);
 }
 
 }  // namespace tpm

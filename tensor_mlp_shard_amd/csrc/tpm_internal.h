@@ -166,4 +166,12 @@ hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int6
 hipError_t launch_reduce(const void *const *parts, int k, int64_t numel, int in_dtype, void *out,
                          int out_dtype, hipStream_t s);
 
+// Partials sum + residual add + RMSNorm, one row per workgroup (cols a multiple of
+// 8, at most kNormMaxCols: 1024 threads x 4 chunks of 8 held in registers).
+constexpr int64_t kNormMaxCols = 32768;
+hipError_t launch_reduce_norm(const void *const *parts, int k, int64_t rows, int64_t cols,
+                              int in_dtype, const void *res_in, void *res_out, int res_dtype,
+                              const void *gamma, float eps, void *y, int out_dtype,
+                              hipStream_t s);
+
 }  // namespace tpm

@@ -146,3 +146,35 @@ def test_reduce_validation(lib):
 def test_python_wrapper_shard_count_mismatch():
     with pytest.raises(ValueError):
         tpm.tensor_parallel_output(None, [1, 2], [1])
+
+
+def test_reduce_add_rmsnorm_validation(lib):
+    f = lib.tp_partials_reduce_add_rmsnorm
+    p = _ptrs(0x1000, 0x2000)
+    r, ro, g, y = (ctypes.c_void_p(a) for a in (0x3000, 0x4000, 0x5000, 0x6000))
+
+    def call(parts=p, k=2, rows=4, cols=64, ind=0, res=r, resout=ro, resd=0, gam=g, eps=1e-6,
+             yy=y, outd=0):
+        return f(parts, k, rows, cols, ind, res, resout, resd, gam, ctypes.c_float(eps), yy, outd,
+                 None)
+
+    assert call(parts=None) == INVALID
+    for kw in ("res", "resout", "gam", "yy"):
+        assert call(**{kw: None}) == INVALID, kw
+    for kw in ("ind", "resd", "outd"):
+        assert call(**{kw: 7}) == INVALID, kw
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(eps=float("inf")) == INVALID
+    assert call(k=0) == SHAPE
+    assert call(k=17, parts=_ptrs(*([0x1000] * 17))) == SHAPE
+    assert call(rows=-1) == SHAPE
+    assert call(rows=1 << 31) == SHAPE
+    for cols in (0, 4, 12, 32776, 1 << 20):
+        assert call(cols=cols) == SHAPE, cols
+    assert call(parts=_ptrs(0x1000, None)) == INVALID
+    assert call(parts=_ptrs(0x1000, 0x2008)) == ALIGN
+    assert call(yy=ctypes.c_void_p(0x6002)) == ALIGN
+    assert call(gam=ctypes.c_void_p(0x5004)) == ALIGN
+    # rows = 0 is a no-op that never touches the device
+    assert call(rows=0) == OK

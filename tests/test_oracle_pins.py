@@ -341,3 +341,103 @@ def test_checker_catches_transposed_second_weight():
     ref = oracle.shard_forward(X, a, b, "silu_gate")
     bad = oracle.shard_forward(X, a, b.T.contiguous(), "silu_gate")
     assert oracle.rel_err(bad, ref) > 2e-2
+
+
+# ------------------------------------------------- partials sum + residual + RMSNorm
+# Pins of oracle.reduce_add_rmsnorm (page "7.4 推理侧并行", section 7.4.2, kernel
+# fusion of the residual add and RMSNorm after the all-reduce; RMSNorm in its
+# textbook form y = h / sqrt(mean(h^2) + eps) * gamma).
+
+def _norm_case(k, rows, cols, seed):
+    parts = [_rand((rows, cols), seed + i) for i in range(k)]
+    res = _rand((rows, cols), seed + 100)
+    gamma = _rand((cols,), seed + 200) + 1.0
+    return parts, res, gamma
+
+
+def _norm_brute(parts, res, gamma, eps):
+    """Element by element with exactly rounded sums (math.fsum), no NumPy reductions."""
+    rows, cols = res.shape
+    H = [[0.0] * cols for _ in range(rows)]
+    Y = [[0.0] * cols for _ in range(rows)]
+    for r in range(rows):
+        for c in range(cols):
+            H[r][c] = math.fsum([float(res[r, c])] + [float(p[r, c]) for p in parts])
+        ms = math.fsum(v * v for v in H[r]) / cols
+        inv = 1.0 / math.sqrt(ms + eps)
+        for c in range(cols):
+            Y[r][c] = H[r][c] * inv * float(gamma[c])
+    return np.array(H), np.array(Y)
+
+
+@pytest.mark.parametrize("k,rows,cols,eps", [(1, 1, 8, 0.0), (2, 3, 16, 1e-6), (3, 2, 24, 0.5),
+                                             (8, 4, 40, 1e-5)])
+def test_norm_brute_force_tiny(k, rows, cols, eps):
+    parts, res, gamma = _norm_case(k, rows, cols, 31 + k)
+    h, y = oracle.reduce_add_rmsnorm(parts, res, gamma, eps)
+    hb, yb = _norm_brute(parts, res, gamma, eps)
+    np.testing.assert_allclose(h, hb, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_norm_constant_row_closed_form():
+    # h = c in every column: mean(h^2) = c^2, so y = c / sqrt(c^2 + eps) * gamma
+    cols, c, eps = 64, 0.75, 0.0625
+    parts = [np.full((1, cols), 0.5), np.full((1, cols), 0.125)]
+    res = np.full((1, cols), 0.125)
+    gamma = np.linspace(-2.0, 2.0, cols)
+    h, y = oracle.reduce_add_rmsnorm(parts, res, gamma, eps)
+    assert np.all(h == c)
+    np.testing.assert_allclose(y[0], c / math.sqrt(c * c + eps) * gamma, rtol=1e-15)
+    # c = 0.75, eps = 0.0625: sqrt(0.5625 + 0.0625) = sqrt(0.625)
+    np.testing.assert_allclose(y[0, -1], 0.75 / math.sqrt(0.625) * 2.0, rtol=1e-15)
+
+
+def test_norm_unit_rms_and_eps_shrink():
+    parts, res, gamma = _norm_case(3, 5, 96, 7)
+    ones = np.ones(96)
+    h, y = oracle.reduce_add_rmsnorm(parts, res, ones, 0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), 1.0, rtol=1e-13)
+    eps = 0.3
+    _, y2 = oracle.reduce_add_rmsnorm(parts, res, ones, eps)
+    ms = np.mean(h * h, axis=1)
+    np.testing.assert_allclose(np.mean(y2 * y2, axis=1), ms / (ms + eps), rtol=1e-13)
+
+
+def test_norm_scale_and_sign_invariance():
+    parts, res, gamma = _norm_case(4, 3, 48, 9)
+    _, y = oracle.reduce_add_rmsnorm(parts, res, gamma, 0.0)
+    _, ys = oracle.reduce_add_rmsnorm([2.5 * p for p in parts], 2.5 * res, gamma, 0.0)
+    _, yn = oracle.reduce_add_rmsnorm([-p for p in parts], -res, gamma, 0.0)
+    np.testing.assert_allclose(ys, y, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(yn, -y, rtol=0, atol=0)
+
+
+def test_norm_residual_out_is_residual_plus_sum():
+    parts, res, gamma = _norm_case(3, 4, 32, 11)
+    h, _ = oracle.reduce_add_rmsnorm(parts, res, gamma, 1e-6)
+    np.testing.assert_array_equal(h, oracle._f64(res) + oracle.partials_sum(parts))
+
+
+def test_norm_pins_catch_planted_mistakes():
+    """Plausible wrong readings of the step, each rejected by one of the pins."""
+    parts, res, gamma = _norm_case(3, 3, 40, 13)
+    eps = 0.01
+    _, ref = _norm_brute(parts, res, gamma, eps)
+    H = oracle._f64(res) + oracle.partials_sum(parts)
+    wrong = {
+        "residual dropped": (H - oracle._f64(res)),
+        "mean subtracted (LayerNorm)": H - H.mean(axis=1, keepdims=True),
+    }
+    for name, hh in wrong.items():
+        y = hh / np.sqrt(np.mean(hh * hh, axis=1, keepdims=True) + eps) * gamma
+        assert np.max(np.abs(y - ref)) > 1e-3, name
+    variants = {
+        "eps outside the root": H / (np.sqrt(np.mean(H * H, axis=1, keepdims=True)) + eps) * gamma,
+        "sum instead of mean": H / np.sqrt(np.sum(H * H, axis=1, keepdims=True) + eps) * gamma,
+        "gamma not applied": H / np.sqrt(np.mean(H * H, axis=1, keepdims=True) + eps),
+        "root-mean over columns - 1": H / np.sqrt(np.sum(H * H, axis=1, keepdims=True)
+                                                  / (H.shape[1] - 1) + eps) * gamma,
+    }
+    for name, y in variants.items():
+        assert np.max(np.abs(y - ref)) > 1e-3, name
