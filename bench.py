@@ -25,6 +25,8 @@ The JSON line also carries
 * ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
 * ``reduce_add_rmsnorm``: the partials sum fused with the residual add and RMSNorm
   that follow it, against the same work in two launches;
+* ``fp8_partials``: the decode partials quantized to FP8 with per-row scales and
+  summed in fp32, against the fp32 sum (time, wire bytes, transport error);
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
   same decode workload.
 
@@ -241,6 +243,15 @@ def _graph_of(fn):
     return g
 
 
+def _repeat(fn, n):
+    """fn(stream) n times in a row: small kernels are captured many to a graph, so a
+    replay's own launch cost does not hide their duration."""
+    def run(sp):
+        for _ in range(n):
+            fn(sp)
+    return run
+
+
 def _time_graph(g, reps, warmup=3):
     import torch
     for _ in range(warmup):
@@ -364,7 +375,7 @@ def run_reduce_norm(lib, dev, reps=200):
     """The step after the all-reduce: the 8 fp32 rank partials summed, the residual
     added and RMSNorm applied, in one kernel (tp_partials_reduce_add_rmsnorm), against
     the same work as two launches (tp_partials_reduce, then the fused call with k = 1
-    on the sum).  Residual, gamma and y in bf16, eps 1e-5; HIP-graph replays."""
+    on the sum).  Residual, gamma and y in bf16, eps 1e-5; many calls per HIP graph."""
     import torch
     out = []
     for rows in (M_DECODE, 2048):
@@ -397,9 +408,10 @@ def run_reduce_norm(lib, dev, reps=200):
                                                           1, sp)
             if rc:
                 raise RuntimeError("reduce / norm failed: %d" % rc)
-        n = max(10, reps if rows <= 64 else reps // 10)
-        gf, gu = _graph_of(fused), _graph_of(unfused)
-        t_f, t_u = _time_graph(gf, n), _time_graph(gu, n)
+        inner = 50 if rows <= 64 else 5
+        n = max(4, reps // inner)
+        gf, gu = _graph_of(_repeat(fused, inner)), _graph_of(_repeat(unfused, inner))
+        t_f, t_u = _time_graph(gf, n) / inner, _time_graph(gu, n) / inner
         del gf, gu
         nbytes = TP * rows * D_MODEL * 4 + 3 * rows * D_MODEL * 2 + D_MODEL * 2
         out.append({"rows": rows, "k": TP, "cols": D_MODEL, "fused_us": round(t_f * 1e6, 2),
@@ -413,7 +425,64 @@ def run_reduce_norm(lib, dev, reps=200):
     return {"points": out,
             "note": "8 fp32 partials + bf16 residual -> bf16 residual_out and bf16 y "
                     "(RMSNorm, eps 1e-5); two_launch = tp_partials_reduce to fp32, then the "
-                    "same fused call with k = 1; HIP-graph replays"}
+                    "same fused call with k = 1; many calls per HIP graph, time per call"}
+
+
+def run_fp8_partials(lib, dev, reps=200):
+    """Low-precision partials: each of the 8 fp32 rank partials of a decode step
+    ([32 x 8192]) quantized to FP8 with per-row scales (tp_partials_quantize_fp8),
+    then the 8 summed in fp32 (tp_partials_reduce_fp8), against the fp32 partials
+    summed directly (tp_partials_reduce), many calls per HIP graph; the transport error is
+    the FP8 sum against the fp32 sum, max-abs over RMS."""
+    import torch
+    rows, cols = M_DECODE, D_MODEL
+    g = torch.Generator().manual_seed(17)
+    parts = [torch.randn(rows, cols, generator=g).to(dev) for _ in range(TP)]
+    qs = [torch.empty(rows, cols, dtype=torch.uint8, device=dev) for _ in range(TP)]
+    ss = [torch.empty(rows, dtype=torch.float32, device=dev) for _ in range(TP)]
+    z8 = torch.empty(rows, cols, device=dev)
+    z32 = torch.empty(rows, cols, device=dev)
+    vp = ctypes.c_void_p
+    parr = (vp * TP)(*[p.data_ptr() for p in parts])
+    qarr = (vp * TP)(*[q.data_ptr() for q in qs])
+    sarr = (vp * TP)(*[s.data_ptr() for s in ss])
+
+    def quant(sp):
+        for p, q, s in zip(parts, qs, ss):
+            rc = lib.tp_partials_quantize_fp8(vp(p.data_ptr()), rows, cols, 0, vp(q.data_ptr()),
+                                              vp(s.data_ptr()), sp)
+            if rc:
+                raise RuntimeError("tp_partials_quantize_fp8 failed: %d" % rc)
+
+    def red8(sp):
+        rc = lib.tp_partials_reduce_fp8(qarr, sarr, TP, rows, cols, vp(z8.data_ptr()), 0, sp)
+        if rc:
+            raise RuntimeError("tp_partials_reduce_fp8 failed: %d" % rc)
+
+    def red32(sp):
+        rc = lib.tp_partials_reduce(parr, TP, rows * cols, 0, vp(z32.data_ptr()), 0, sp)
+        if rc:
+            raise RuntimeError("tp_partials_reduce failed: %d" % rc)
+    inner = 25
+    gq, g8, g32 = (_graph_of(_repeat(f, inner)) for f in (quant, red8, red32))
+    n = max(4, reps // inner)
+    t_q = _time_graph(gq, n) / inner / TP
+    t_8, t_32 = _time_graph(g8, n) / inner, _time_graph(g32, n) / inner
+    del gq, g8, g32
+    torch.cuda.synchronize()
+    err = float((z8 - z32).abs().max() / z32.pow(2).mean().sqrt())
+    out = {"rows": rows, "cols": cols, "k": TP,
+           "quantize_us_per_partial": round(t_q * 1e6, 2), "reduce_fp8_us": round(t_8 * 1e6, 2),
+           "reduce_fp32_us": round(t_32 * 1e6, 2),
+           "wire_bytes_per_partial": {"fp32": rows * cols * 4, "bf16": rows * cols * 2,
+                                      "fp8_e4m3_plus_row_scales": rows * cols + rows * 4},
+           "transport_err_max_abs_over_rms": round(err, 5),
+           "note": "partials N(0,1) fp32; quantize = one partial; reduce_fp8 dequantizes the 8 "
+                   "FP8 partials with their row scales and sums in fp32; many calls per HIP "
+                   "graph, time per call"}
+    log("fp8 partials: quantize %.2f us/partial, reduce fp8 %.2f us, reduce fp32 %.2f us, "
+        "err %.4f" % (t_q * 1e6, t_8 * 1e6, t_32 * 1e6, err))
+    return out
 
 
 def cpu_baseline(host_inputs, budget_s=12.0):
@@ -566,10 +635,12 @@ def main():
         log("tensor-parallel degree sweep ...")
         sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
 
-    reduce_norm = None
+    reduce_norm = fp8 = None
     if not args.no_sweep:
         log("partials sum + residual + RMSNorm ...")
         reduce_norm = run_reduce_norm(lib, dev)
+        log("fp8 partials ...")
+        fp8 = run_fp8_partials(lib, dev)
 
     if args.calib_copy:
         calib_copy(dev)
@@ -602,6 +673,7 @@ def main():
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,
         "reduce_add_rmsnorm": reduce_norm,
+        "fp8_partials": fp8,
         "cpu_baseline": cpu,
         "device": props.name,
         "source_hash": kernel_source_hash(),

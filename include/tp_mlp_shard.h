@@ -191,6 +191,45 @@ tpm_status tp_partials_reduce_add_rmsnorm(const void *const *partials_dev, int32
                                           int32_t res_dtype, const void *gamma_dev, float eps,
                                           void *y_dev, int32_t out_dtype, void *stream);
 
+/* Low-precision partials (page "7.4 推理侧并行", section 7.4.2, communication
+ * quantization: partials may travel in FP8 with a per-token scale, but the sum is
+ * done in high precision after dequantizing).  FP8 here is OCP E4M3 (1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, codes
+ * 0x7f / 0xff are NaN, largest finite value 448); the pages do not fix the layout.
+ *
+ * Quantize one partial, per row r of [rows x cols]:
+ *   amax_r    = max_c |x[r][c]|
+ *   scale[r]  = amax_r / 448                 (fp32, correctly rounded; 1 if amax_r = 0)
+ *   q[r][c]   = E4M3(x[r][c] * (448 / amax_r)), both fp32 operations correctly
+ *               rounded, the code rounded to nearest (ties to even) and saturated to
+ *               +-448; all zero when amax_r = 0.
+ * A row holding NaN or infinity gives unspecified codes and scale.
+ *
+ *   partial_dev  [rows x cols] of in_dtype (TPM_F32 or TPM_BF16).
+ *   rows         >= 0 (0 is a no-op), at most 2^31 - 1.
+ *   cols         a multiple of 16, 16 <= cols <= 32768.
+ *   q_dev        [rows x cols] bytes (E4M3 codes).
+ *   scale_dev    [rows] fp32.
+ * Asynchronous on `stream`; allocates nothing. */
+tpm_status tp_partials_quantize_fp8(const void *partial_dev, int64_t rows, int64_t cols,
+                                    int32_t in_dtype, void *q_dev, float *scale_dev,
+                                    void *stream);
+
+/* Sum k quantized partials with fp32 accumulation, in rank order:
+ *   out[r][c] = ((d_0 + d_1) + ...) + d_{k-1},  d_i = value(q_i[r][c]) * scale_i[r]
+ * (each product rounded to fp32).
+ *
+ *   q_dev      host array of k device pointers, each [rows x cols] E4M3 codes.
+ *   scale_dev  host array of k device pointers, each [rows] fp32.
+ *   k          1 <= k <= 16.
+ *   rows, cols cols a multiple of 16 (>= 16), rows >= 0 (0 is a no-op).
+ *   out_dev    [rows x cols] of out_dtype (TPM_F32 or TPM_BF16); must not overlap
+ *              the inputs.
+ * Bitwise reproducible from call to call.  Asynchronous on `stream`. */
+tpm_status tp_partials_reduce_fp8(const void *const *q_dev, const float *const *scale_dev,
+                                  int32_t k, int64_t rows, int64_t cols, void *out_dev,
+                                  int32_t out_dtype, void *stream);
+
 /* Free a handle and its device memory (waits for the device first).  NULL is OK. */
 tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
 

@@ -17,7 +17,11 @@ It follows the pages' statement of the method:
   by the up branch;
 * page "7.4 推理侧并行", section 7.4.2 (kernel fusion after the all-reduce): the
   residual add and RMSNorm that follow the sum (``reduce_add_rmsnorm``; RMSNorm in
-  its textbook form, which the pages name without defining).
+  its textbook form, which the pages name without defining);
+* same section (communication quantization): partials travel as FP8 with a
+  per-token scale and are summed in high precision (``e4m3_value``,
+  ``e4m3_encode``, ``quantize_fp8``, ``reduce_fp8``).  FP8 is the OCP E4M3 format,
+  written here from its definition (the pages name FP8 without fixing it).
 
 Activation names: ``"tanh"``, ``"silu_gate"``, ``"identity"``.  For ``silu_gate``
 a shard's first weight has ``2F`` columns: the ``F`` gate columns, then the ``F``
@@ -181,6 +185,72 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float):
     ms = np.mean(h * h, axis=1, keepdims=True)
     y = h / np.sqrt(ms + float(eps)) * g[None, :]
     return h, y
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 byte: sign bit, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal (m / 8 * 2^-6); 0x7f and 0xff are NaN."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_POS = np.array([e4m3_value(c) for c in range(0x7F)], dtype=np.float64)  # codes 0..126
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to the even code), saturating to
+    +-448; NaN gives 0x7f.  Works on the exact values given (no rescaling): the
+    magnitude is located in the table of the 127 non-negative finite values and
+    the nearer neighbour is taken."""
+    a = np.asarray(x, dtype=np.float64)
+    mag = np.abs(a)
+    nan = np.isnan(a)
+    m = np.where(nan, 0.0, mag)
+    hi = np.clip(np.searchsorted(_E4M3_POS, m, side="left"), 1, len(_E4M3_POS) - 1)
+    lo = hi - 1
+    dl = m - _E4M3_POS[lo]
+    dh = _E4M3_POS[hi] - m
+    code = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(m >= _E4M3_POS[-1], 0x7E, code)
+    sign = np.where(np.signbit(a), 0x80, 0)
+    out = np.where(nan, 0x7F, sign | code)
+    return out.astype(np.uint8)
+
+
+def quantize_fp8(x):
+    """Per-row FP8 quantization of a partial [rows, cols] given in fp32 or bf16:
+    amax per row, scale = amax / 448 and codes of x * (448 / amax), each of the
+    two divisions and the product taken in fp32 with correct rounding (the
+    precision the codes are decided in).  Zero rows: scale 1, all codes 0.
+    Returns (codes uint8 [rows, cols], scales float32 [rows])."""
+    X = np.asarray(_f64(x), dtype=np.float32)  # exact: the inputs are fp32 or bf16
+    rows = X.shape[0]
+    codes = np.zeros(X.shape, dtype=np.uint8)
+    scales = np.ones(rows, dtype=np.float32)
+    for r in range(rows):
+        amax = np.float32(np.max(np.abs(X[r]))) if X.shape[1] else np.float32(0)
+        if not amax > 0:
+            continue
+        inv = np.float32(448.0) / amax
+        scales[r] = amax / np.float32(448.0)
+        codes[r] = e4m3_encode((X[r] * inv).astype(np.float32))
+    return codes, scales
+
+
+def reduce_fp8(codes, scales) -> np.ndarray:
+    """Sum over ranks of value(code_i) * scale_i[row], in fp64, rank order."""
+    table = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+    total = None
+    for q, s in zip(codes, scales):
+        d = table[np.asarray(q, dtype=np.uint8)] * np.asarray(s, dtype=np.float64)[:, None]
+        total = d if total is None else total + d
+    return total
 
 
 def rel_err(got, ref) -> float:

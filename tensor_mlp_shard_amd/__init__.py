@@ -8,7 +8,8 @@ The functions carry the names of the C ABI (``include/tp_mlp_shard.h``):
 
 * ``tp_mlp_shard_plan``, ``tp_mlp_shard_create``, ``tp_mlp_shard_fwd``,
   ``tp_mlp_shard_destroy``, ``tp_partials_reduce``,
-  ``tp_partials_reduce_add_rmsnorm``, ``tpm_status_str``,
+  ``tp_partials_reduce_add_rmsnorm``, ``tp_partials_quantize_fp8``,
+  ``tp_partials_reduce_fp8``, ``tpm_status_str``,
   ``tp_mlp_shard_set_timing_events``;
 
 plus two conveniences: ``Shard`` (one rank's handle) and
@@ -23,7 +24,8 @@ import os
 
 __all__ = [
     "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
-    "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
+    "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tp_partials_quantize_fp8",
+    "tp_partials_reduce_fp8", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
     "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
 ]
 
@@ -83,6 +85,11 @@ def capi():
     lib.tp_partials_reduce_add_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i32, vp, vp,
                                                    i32, vp, ctypes.c_float, vp, i32, vp]
     lib.tp_partials_reduce_add_rmsnorm.restype = ctypes.c_int
+    lib.tp_partials_quantize_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.tp_partials_quantize_fp8.restype = ctypes.c_int
+    lib.tp_partials_reduce_fp8.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i64,
+                                           vp, i32, vp]
+    lib.tp_partials_reduce_fp8.restype = ctypes.c_int
     lib.tp_mlp_shard_destroy.argtypes = [vp]
     lib.tp_mlp_shard_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
@@ -203,6 +210,44 @@ def tp_partials_reduce_add_rmsnorm(partials, residual, gamma, eps, y, residual_o
         _dev_ptr(residual_out, "residual_out"), _dtype_code(residual.dtype),
         _dev_ptr(gamma, "gamma"), float(eps), _dev_ptr(y, "y"), _dtype_code(y.dtype),
         _stream_ptr(stream)), "tp_partials_reduce_add_rmsnorm")
+
+
+def tp_partials_quantize_fp8(partial, q, scale, stream=None) -> None:
+    """FP8 (E4M3) codes of a partial [rows, cols] with one fp32 scale per row:
+    q uint8 [rows, cols], scale float32 [rows] (see the C header)."""
+    torch = _torch()
+    if partial.dim() != 2:
+        raise ValueError("partial must be [rows, cols]")
+    rows, cols = partial.shape
+    if tuple(q.shape) != (rows, cols) or q.dtype != torch.uint8:
+        raise ValueError("q must be uint8 [rows, cols]")
+    if tuple(scale.shape) != (rows,) or scale.dtype != torch.float32:
+        raise ValueError("scale must be float32 [rows]")
+    _check(capi().tp_partials_quantize_fp8(_dev_ptr(partial, "partial"), rows, cols,
+                                           _dtype_code(partial.dtype), _dev_ptr(q, "q"),
+                                           _dev_ptr(scale, "scale"), _stream_ptr(stream)),
+           "tp_partials_quantize_fp8")
+
+
+def tp_partials_reduce_fp8(qs, scales, out, stream=None) -> None:
+    """out = sum over ranks of value(q_i) * scale_i[row], fp32 accumulation."""
+    torch = _torch()
+    qs, scales = list(qs), list(scales)
+    if not qs or len(qs) != len(scales):
+        raise ValueError("need matching, non-empty lists of codes and scales")
+    rows, cols = qs[0].shape
+    for q, s in zip(qs, scales):
+        if tuple(q.shape) != (rows, cols) or q.dtype != torch.uint8:
+            raise ValueError("codes must be uint8 [rows, cols]")
+        if tuple(s.shape) != (rows,) or s.dtype != torch.float32:
+            raise ValueError("scales must be float32 [rows]")
+    if tuple(out.shape) != (rows, cols):
+        raise ValueError("out must be [rows, cols]")
+    qa = (ctypes.c_void_p * len(qs))(*[_dev_ptr(q, "q").value for q in qs])
+    sa = (ctypes.c_void_p * len(qs))(*[_dev_ptr(s, "scale").value for s in scales])
+    _check(capi().tp_partials_reduce_fp8(qa, sa, len(qs), rows, cols, _dev_ptr(out, "out"),
+                                         _dtype_code(out.dtype), _stream_ptr(stream)),
+           "tp_partials_reduce_fp8")
 
 
 def tp_mlp_shard_destroy(handle: int) -> None:

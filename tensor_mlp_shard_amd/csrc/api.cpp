@@ -314,6 +314,37 @@ tpm_status tp_partials_reduce_add_rmsnorm(const void *const *partials_dev, int32
                                      out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+tpm_status tp_partials_quantize_fp8(const void *partial_dev, int64_t rows, int64_t cols,
+                                    int32_t in_dtype, void *q_dev, float *scale_dev,
+                                    void *stream) {
+  if (!partial_dev || !q_dev || !scale_dev) return TPM_ERR_INVALID_ARG;
+  if (in_dtype != TPM_F32 && in_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (rows < 0 || rows > 0x7fffffff || cols < 16 || cols % 16 || cols > kFp8MaxCols)
+    return TPM_ERR_SHAPE;
+  if (!aligned(partial_dev) || !aligned(q_dev) || !aligned(scale_dev)) return TPM_ERR_ALIGN;
+  if (rows == 0) return TPM_OK;
+  return from_hip(launch_quant_fp8(partial_dev, rows, cols, in_dtype, q_dev, scale_dev,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+tpm_status tp_partials_reduce_fp8(const void *const *q_dev, const float *const *scale_dev,
+                                  int32_t k, int64_t rows, int64_t cols, void *out_dev,
+                                  int32_t out_dtype, void *stream) {
+  if (!q_dev || !scale_dev || !out_dev) return TPM_ERR_INVALID_ARG;
+  if (out_dtype != TPM_F32 && out_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxParts || rows < 0 || cols < 16 || cols % 16 ||
+      rows > (int64_t(1) << 40) / cols)
+    return TPM_ERR_SHAPE;
+  for (int i = 0; i < k; ++i) {
+    if (!q_dev[i] || !scale_dev[i]) return TPM_ERR_INVALID_ARG;
+    if (!aligned(q_dev[i])) return TPM_ERR_ALIGN;
+  }
+  if (!aligned(out_dev)) return TPM_ERR_ALIGN;
+  if (rows == 0) return TPM_OK;
+  return from_hip(launch_reduce_fp8(q_dev, scale_dev, k, rows, cols, out_dev, out_dtype,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 tpm_status tp_mlp_shard_destroy(tpm_shard_t handle) {
   Shard *h = reinterpret_cast<Shard *>(handle);
   if (!h) return TPM_OK;

@@ -174,4 +174,13 @@ hipError_t launch_reduce_norm(const void *const *parts, int k, int64_t rows, int
                               const void *gamma, float eps, void *y, int out_dtype,
                               hipStream_t s);
 
+// FP8 (E4M3) partials with one scale per row: quantize one partial, and the
+// rank-order fp32 sum of k quantized partials.  cols a multiple of 16; the
+// quantizer holds a row in registers (1024 threads x 2 chunks of 16).
+constexpr int64_t kFp8MaxCols = 32768;
+hipError_t launch_quant_fp8(const void *x, int64_t rows, int64_t cols, int in_dtype, void *q,
+                            float *scale, hipStream_t s);
+hipError_t launch_reduce_fp8(const void *const *q, const float *const *scales, int k, int64_t rows,
+                             int64_t cols, void *out, int out_dtype, hipStream_t s);
+
 }  // namespace tpm

@@ -178,3 +178,27 @@ def test_reduce_add_rmsnorm_validation(lib):
     assert call(gam=ctypes.c_void_p(0x5004)) == ALIGN
     # rows = 0 is a no-op that never touches the device
     assert call(rows=0) == OK
+
+
+def test_fp8_validation(lib):
+    qf, rf = lib.tp_partials_quantize_fp8, lib.tp_partials_reduce_fp8
+    x, q, s = (ctypes.c_void_p(a) for a in (0x1000, 0x2000, 0x3000))
+    assert qf(None, 4, 64, 0, q, s, None) == INVALID
+    assert qf(x, 4, 64, 0, None, s, None) == INVALID
+    assert qf(x, 4, 64, 0, q, None, None) == INVALID
+    assert qf(x, 4, 64, 9, q, s, None) == INVALID
+    for cols in (0, 8, 24, 32784):
+        assert qf(x, 4, cols, 0, q, s, None) == SHAPE, cols
+    assert qf(x, -1, 64, 0, q, s, None) == SHAPE
+    assert qf(ctypes.c_void_p(0x1004), 4, 64, 0, q, s, None) == ALIGN
+    assert qf(x, 0, 64, 0, q, s, None) == OK
+    qs, ss, out = _ptrs(0x1000, 0x2000), _ptrs(0x3000, 0x4000), ctypes.c_void_p(0x5000)
+    assert rf(None, ss, 2, 4, 64, out, 0, None) == INVALID
+    assert rf(qs, None, 2, 4, 64, out, 0, None) == INVALID
+    assert rf(qs, ss, 2, 4, 64, None, 0, None) == INVALID
+    assert rf(qs, ss, 2, 4, 64, out, 3, None) == INVALID
+    assert rf(qs, ss, 0, 4, 64, out, 0, None) == SHAPE
+    assert rf(qs, ss, 2, 4, 40, out, 0, None) == SHAPE
+    assert rf(qs, _ptrs(0x3000, None), 2, 4, 64, out, 0, None) == INVALID
+    assert rf(_ptrs(0x1000, 0x2001), ss, 2, 4, 64, out, 0, None) == ALIGN
+    assert rf(qs, ss, 2, 0, 64, out, 0, None) == OK

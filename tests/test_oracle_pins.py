@@ -441,3 +441,77 @@ def test_norm_pins_catch_planted_mistakes():
     }
     for name, y in variants.items():
         assert np.max(np.abs(y - ref)) > 1e-3, name
+
+
+# ------------------------------------------------------------------ FP8 partials
+# Pins of the E4M3 codec and of the per-row quantizer (page "7.4 推理侧并行",
+# section 7.4.2, communication quantization; E4M3 values from the OCP FP8 format).
+
+def test_e4m3_known_codes():
+    known = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0xC0: -2.0, 0x7E: 448.0,
+             0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x77: 240.0,
+             0x30: 0.5, 0xB8: -1.0, 0x6F: 120.0}
+    for c, v in known.items():
+        assert oracle.e4m3_value(c) == v, hex(c)
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    assert math.copysign(1.0, oracle.e4m3_value(0x80)) == -1.0
+
+
+def test_e4m3_roundtrip_and_monotonic():
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = [oracle.e4m3_value(c) for c in finite]
+    enc = oracle.e4m3_encode(np.array(vals))
+    for c, e, v in zip(finite, enc, vals):
+        if v == 0.0:
+            assert e in (0x00, 0x80)
+        else:
+            assert e == c, (hex(c), hex(int(e)))
+    pos = [oracle.e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 1.5 * 2.0 ** -9: 0x02, 0.5 * 2.0 ** -9: 0x00,
+             2.5 * 2.0 ** -9: 0x02, 432.0: 0x7E, 416.0: 0x7D, 400.0: 0x7C, 448.0: 0x7E, 463.9: 0x7E,
+             1e9: 0x7E, -1e9: 0xFE, -1.0625: 0xB8, 1.07: 0x39}
+    got = oracle.e4m3_encode(np.array(list(cases)))
+    for (x, c), g in zip(cases.items(), got):
+        assert g == c, (x, hex(int(g)), hex(c))
+
+
+def test_quantize_fp8_rows():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(6, 64, generator=g)
+    x[2] = 0.0
+    x[4] *= 1e-3
+    codes, scales = oracle.quantize_fp8(x)
+    X = x.numpy()
+    for r in range(6):
+        if r == 2:
+            assert scales[r] == 1.0 and np.all(codes[r] == 0)
+            continue
+        amax = np.float32(np.max(np.abs(X[r])))
+        assert scales[r] == np.float32(amax / np.float32(448.0))
+        # the largest magnitude lands on +-448
+        j = int(np.argmax(np.abs(X[r])))
+        assert codes[r, j] & 0x7F == 0x7E
+        # every element within half a grid spacing (relative 2^-4) of its code
+        deq = np.array([oracle.e4m3_value(int(c)) for c in codes[r]]) * float(scales[r])
+        assert np.all(np.abs(deq - X[r]) <= np.abs(X[r]) * 2.0 ** -4 + 2.0 ** -10 * float(scales[r]))
+
+
+def test_reduce_fp8_is_sum_of_dequantized():
+    g = torch.Generator().manual_seed(4)
+    parts = [torch.randn(3, 32, generator=g) for _ in range(4)]
+    qs = [oracle.quantize_fp8(p) for p in parts]
+    z = oracle.reduce_fp8([q for q, _ in qs], [s for _, s in qs])
+    want = sum(np.array([[oracle.e4m3_value(int(c)) for c in row] for row in q]) * s[:, None].astype(np.float64)
+               for q, s in qs)
+    np.testing.assert_array_equal(z, want)
+    # and it is within the E4M3 rounding of the exact sum: each partial element is
+    # off by at most half a grid spacing, 2^-4 of its magnitude (2^-10 scale units
+    # in the subnormal range)
+    exact = oracle.partials_sum(parts)
+    bound = sum(np.abs(oracle._f64(p)) * 2.0 ** -4 + 2.0 ** -10 * s[:, None].astype(np.float64)
+                for p, (_, s) in zip(parts, qs))
+    assert np.all(np.abs(z - exact) <= bound)
