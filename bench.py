@@ -23,6 +23,8 @@ The JSON line also carries
 * ``tp_sweep``: single-rank shards at tensor-parallel degree 1, 2, 4, 8 (per-rank
   hidden width 28672 / k) and M in {1, 8, 32, 64, 4096}, each against its roofline;
 * ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
+* ``attention_projections``: the attention block's column-parallel QKV and
+  row-parallel output projections of the same model (decode and prefill shapes);
 * ``reduce_add_rmsnorm``: the partials sum fused with the residual add and RMSNorm
   that follow it, against the same work in two launches;
 * ``fp8_partials``: the decode partials quantized to FP8 with per-row scales and
@@ -371,6 +373,67 @@ def run_sweep(tpm, lib, dev, host_shards8, log_fn=log):
                     "calls replayed from a HIP graph over all tp ranks in turn"}, all_shards
 
 
+def run_attention_projections(tpm, lib, synth, dev):
+    """The attention block's projections of all 8 TP=8 ranks of the 70B-class model
+    (64 query heads and 8 KV heads of width 128): per rank the column-parallel QKV
+    shard [8192 x 1280] (bf16 out) and the row-parallel output shard [1024 x 8192]
+    (fp32 partial), one after another, at the decode shape (M = 32: weight GB/s; the
+    16 shards hold 302 MB, more than the last-level cache) and at the prefill shape
+    (M = 8192, rank 0: TFLOP/s).  Calls captured in HIP graphs."""
+    import torch
+    spec = synth.AttentionSpec()
+    res = {}
+    for M in (M_DECODE, M_PREFILL):
+        ranks = range(TP) if M == M_DECODE else range(1)
+        projs, calls, wbytes, flops = [], [], 0, 0
+        x = synth.tokens(M).to(dev)
+        for r in ranks:
+            wqkv, wo = spec.shard(r, TP)
+            pq = tpm.Projection(wqkv.to(dev), max_tokens=M, out_dtype=torch.bfloat16)
+            po = tpm.Projection(wo.to(dev), max_tokens=M, out_dtype=torch.float32)
+            y = torch.empty(M, wqkv.shape[1], dtype=torch.bfloat16, device=dev)
+            a = torch.empty(M, wo.shape[0], dtype=torch.bfloat16, device=dev).normal_()
+            p = torch.empty(M, D_MODEL, dtype=torch.float32, device=dev)
+            projs += [pq, po]
+            calls.append((pq.handle, x, y))
+            calls.append((po.handle, a, p))
+            wbytes += (wqkv.numel() + wo.numel()) * 2
+            flops += 2 * M * (wqkv.numel() + wo.numel())
+        vp = ctypes.c_void_p
+        args = [(vp(h), vp(xx.data_ptr()), ctypes.c_int64(M), vp(yy.data_ptr()))
+                for h, xx, yy in calls]
+
+        def step(sp, args=args):
+            for a_ in args:
+                rc = lib.tp_proj_fwd(*a_, sp)
+                if rc:
+                    raise RuntimeError("tp_proj_fwd failed: %d" % rc)
+        g = _graph_of(step)
+        t = _time_graph(g, 50 if M == M_DECODE else 10)
+        del g
+        if M == M_DECODE:
+            res["decode"] = {"M": M, "ranks": TP, "us_per_step": round(t * 1e6, 2),
+                             "weight_bytes": wbytes, "GBs": round(wbytes / t / 1e9, 1),
+                             "frac_of_hbm_peak": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+            log("attention projections, decode (8 ranks QKV + O, M=32): %.2f us, %.1f GB/s"
+                % (t * 1e6, wbytes / t / 1e9))
+        else:
+            res["prefill"] = {"M": M, "ranks": 1, "us_per_step": round(t * 1e6, 2),
+                              "flops": flops, "TFLOPs": round(flops / t / 1e12, 1),
+                              "frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            log("attention projections, prefill (rank 0 QKV + O, M=8192): %.2f us, %.1f TFLOP/s"
+                % (t * 1e6, flops / t / 1e12))
+        for pr in projs:
+            pr.close()
+        del x
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    res["note"] = ("Llama-3-70B-style heads: per rank 8 query heads + 1 K + 1 V head of width "
+                   "128 (QKV shard [8192 x 1280]) and Wo rows [1024 x 8192]; the attention "
+                   "itself is not part of this library")
+    return res
+
+
 def run_reduce_norm(lib, dev, reps=200):
     """The step after the all-reduce: the 8 fp32 rank partials summed, the residual
     added and RMSNorm applied, in one kernel (tp_partials_reduce_add_rmsnorm), against
@@ -635,8 +698,10 @@ def main():
         log("tensor-parallel degree sweep ...")
         sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
 
-    reduce_norm = fp8 = None
+    reduce_norm = fp8 = attn = None
     if not args.no_sweep:
+        log("attention projections ...")
+        attn = run_attention_projections(tpm, lib, synth, dev)
         log("partials sum + residual + RMSNorm ...")
         reduce_norm = run_reduce_norm(lib, dev)
         log("fp8 partials ...")
@@ -672,6 +737,7 @@ def main():
         "prefill": prefill,
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,
+        "attention_projections": attn,
         "reduce_add_rmsnorm": reduce_norm,
         "fp8_partials": fp8,
         "cpu_baseline": cpu,

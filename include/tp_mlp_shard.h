@@ -233,6 +233,53 @@ tpm_status tp_partials_reduce_fp8(const void *const *q_dev, const float *const *
 /* Free a handle and its device memory (waits for the device first).  NULL is OK. */
 tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
 
+/* Single tensor-parallel projections, Y = X W on one rank's shard of W.
+ *
+ * Page "大模型推理系统揭秘（07）Multi-GPU", section 1.2.4: in the attention block
+ * the Q, K and V projections are column-parallel (each GPU holds some heads), the
+ * attention is computed locally, and the output projection is row-parallel, its
+ * rank partials summed by one all-reduce.  The attention itself is not part of
+ * this library; the two projections around it are:
+ *   - column-parallel QKV: W = the rank's columns of [Wq | Wk | Wv] ([d x n_i]),
+ *     Y = [M x n_i] (bf16 for the local attention);
+ *   - row-parallel output: W = the rank's rows of Wo ([q_i x d]), X = the rank's
+ *     attention output [M x q_i], Y = its fp32 partial [M x d], summed over ranks
+ *     with tp_partials_reduce.
+ *
+ *   in_features   K: width of X and rows of W.
+ *   out_features  N: columns of W and of Y.
+ *   max_tokens    largest M a fwd call may pass.
+ *   in_dtype      dtype of X and W (TPM_F32 or TPM_BF16); out_dtype: dtype of Y.
+ *   path          tpm_path (AUTO: M <= stream_max_tokens streams the weight).
+ * Constraints (TPM_ERR_SHAPE otherwise): K, N >= 1, max_tokens >= 0; for TPM_BF16
+ * input K must be a multiple of 64.  N has no multiple constraint. */
+typedef struct tpm_proj_desc {
+  int64_t in_features;
+  int64_t out_features;
+  int64_t max_tokens;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t path;
+  int32_t reserved;
+} tpm_proj_desc;
+
+typedef struct tpm_proj *tpm_proj_t;
+
+/* Create a projection handle: allocate its device memory on the current device,
+ * repack W_dev ([K x N] row-major, in_dtype) and wait for `stream`.  The handle owns
+ * its copy; W_dev may be freed once create returns.  On error *out is NULL. */
+tpm_status tp_proj_create(const tpm_proj_desc *desc, const void *W_dev, void *stream,
+                          tpm_proj_t *out);
+
+/* Y_dev = X_dev W with fp32 accumulation.  X_dev [M x K] in_dtype, Y_dev [M x N]
+ * out_dtype, fully overwritten; 0 <= M <= max_tokens (0 is a no-op).  Asynchronous
+ * on `stream`, allocates nothing (graph-capturable); one handle on one stream at a
+ * time.  X_dev and Y_dev must not overlap. */
+tpm_status tp_proj_fwd(tpm_proj_t h, const void *X_dev, int64_t M, void *Y_dev, void *stream);
+
+/* Free a projection handle (waits for the device first).  NULL is OK. */
+tpm_status tp_proj_destroy(tpm_proj_t h);
+
 /* Timing hook for profiling.  When `events` is non-NULL, every later fwd call on
  * this handle attaches events[2j] and events[2j+1] to its j-th kernel launch, for
  * j < kernels_per_fwd: they record the start and the end of that kernel's

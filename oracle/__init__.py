@@ -18,7 +18,10 @@ It follows the pages' statement of the method:
 * page "7.4 推理侧并行", section 7.4.2 (kernel fusion after the all-reduce): the
   residual add and RMSNorm that follow the sum (``reduce_add_rmsnorm``; RMSNorm in
   its textbook form, which the pages name without defining);
-* same section (communication quantization): partials travel as FP8 with a
+* page "大模型推理系统揭秘（07）Multi-GPU", section 1.2.4: the attention block's
+  QKV projection is column-parallel and its output projection row-parallel
+  (``projection``, one matrix product);
+* page "7.4 推理侧并行", section 7.4.2 (communication quantization): partials travel as FP8 with a
   per-token scale and are summed in high precision (``e4m3_value``,
   ``e4m3_encode``, ``quantize_fp8``, ``reduce_fp8``).  FP8 is the OCP E4M3 format,
   written here from its definition (the pages name FP8 without fixing it).
@@ -169,6 +172,16 @@ def unsplit_output(x, a_shards, b_shards, activation: str = "tanh") -> np.ndarra
     """The same MLP computed without splitting: one shard holding all hidden features."""
     A, B = unsplit_weights(a_shards, b_shards, activation)
     return shard_forward(x, A, B, activation)
+
+
+def projection(x, w) -> np.ndarray:
+    """One projection ``x @ w`` in fp64 (page "大模型推理系统揭秘（07）Multi-GPU",
+    section 1.2.2: Y = XW; column shards of W give column blocks of Y, row shards of
+    W with the matching column blocks of X give partials that sum to Y)."""
+    X, W = _f64(x), _f64(w)
+    if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[0]:
+        raise ValueError("shapes %s and %s do not chain" % (X.shape, W.shape))
+    return X @ W
 
 
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float):

@@ -9,10 +9,12 @@ The functions carry the names of the C ABI (``include/tp_mlp_shard.h``):
 * ``tp_mlp_shard_plan``, ``tp_mlp_shard_create``, ``tp_mlp_shard_fwd``,
   ``tp_mlp_shard_destroy``, ``tp_partials_reduce``,
   ``tp_partials_reduce_add_rmsnorm``, ``tp_partials_quantize_fp8``,
-  ``tp_partials_reduce_fp8``, ``tpm_status_str``,
+  ``tp_partials_reduce_fp8``, ``tp_proj_create``, ``tp_proj_fwd``,
+  ``tp_proj_destroy``, ``tpm_status_str``,
   ``tp_mlp_shard_set_timing_events``;
 
-plus two conveniences: ``Shard`` (one rank's handle) and
+plus conveniences: ``Shard`` (one rank's MLP handle), ``Projection`` (one rank's
+shard of a single projection, e.g. the attention QKV or output projection) and
 ``tensor_parallel_output(x, a_shards, b_shards, activation="tanh")``, the pages'
 statement Z = sum_i act(x @ a_i) @ b_i (page "LLM 推理并行化：先找瓶颈，再决定怎么
 切", section 三.2), which raises ``ValueError`` when the shard lists differ in length.
@@ -25,7 +27,8 @@ import os
 __all__ = [
     "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
     "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tp_partials_quantize_fp8",
-    "tp_partials_reduce_fp8", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
+    "tp_partials_reduce_fp8", "tp_proj_create", "tp_proj_fwd", "tp_proj_destroy",
+    "Projection", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
     "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
 ]
 
@@ -50,6 +53,13 @@ class TpmPlanInfo(ctypes.Structure):
     _fields_ = [("packed_weight_bytes", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("ffn_padded", ctypes.c_int64), ("stream_max_tokens", ctypes.c_int64),
                 ("kernels_per_fwd", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class TpmProjDesc(ctypes.Structure):
+    _fields_ = [("in_features", ctypes.c_int64), ("out_features", ctypes.c_int64),
+                ("max_tokens", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class TpmError(RuntimeError):
@@ -90,6 +100,12 @@ def capi():
     lib.tp_partials_reduce_fp8.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i64,
                                            vp, i32, vp]
     lib.tp_partials_reduce_fp8.restype = ctypes.c_int
+    lib.tp_proj_create.argtypes = [ctypes.POINTER(TpmProjDesc), vp, vp, ctypes.POINTER(vp)]
+    lib.tp_proj_create.restype = ctypes.c_int
+    lib.tp_proj_fwd.argtypes = [vp, vp, i64, vp, vp]
+    lib.tp_proj_fwd.restype = ctypes.c_int
+    lib.tp_proj_destroy.argtypes = [vp]
+    lib.tp_proj_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_destroy.argtypes = [vp]
     lib.tp_mlp_shard_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
@@ -313,6 +329,66 @@ class Shard:
     def close(self):
         if getattr(self, "handle", None):
             tp_mlp_shard_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tp_proj_create(desc: TpmProjDesc, W, stream=None) -> int:
+    """Create a projection handle from a device tensor W [in_features, out_features]."""
+    h = ctypes.c_void_p()
+    _check(capi().tp_proj_create(ctypes.byref(desc), _dev_ptr(W, "W"), _stream_ptr(stream),
+                                 ctypes.byref(h)), "tp_proj_create")
+    return h.value
+
+
+def tp_proj_fwd(handle: int, X, M: int, Y, stream=None) -> None:
+    _check(capi().tp_proj_fwd(ctypes.c_void_p(handle), _dev_ptr(X, "X"), int(M), _dev_ptr(Y, "Y"),
+                              _stream_ptr(stream)), "tp_proj_fwd")
+
+
+def tp_proj_destroy(handle: int) -> None:
+    _check(capi().tp_proj_destroy(ctypes.c_void_p(handle)), "tp_proj_destroy")
+
+
+class Projection:
+    """One rank's shard of a single projection, Y = X W (the handle owns a packed
+    copy of W).  For the attention block: the column shard of [Wq | Wk | Wv] with
+    bf16 output, or the row shard of Wo with an fp32 partial output."""
+
+    def __init__(self, w, max_tokens=None, out_dtype=None, path="auto", stream=None):
+        torch = _torch()
+        if w.dim() != 2:
+            raise ValueError("w must be [in_features, out_features]")
+        self.in_features, self.out_features = w.shape
+        self.in_dtype = w.dtype
+        self.out_dtype = out_dtype if out_dtype is not None else torch.float32
+        self.max_tokens = int(max_tokens) if max_tokens is not None else 8192
+        self.desc = TpmProjDesc(int(self.in_features), int(self.out_features), self.max_tokens,
+                                _dtype_code(w.dtype), _dtype_code(self.out_dtype), PATH[path], 0)
+        self.handle = tp_proj_create(self.desc, w, stream)
+
+    def forward(self, x, out=None, stream=None):
+        torch = _torch()
+        if x.dim() != 2 or x.shape[1] != self.in_features or x.dtype != self.in_dtype:
+            raise ValueError("x must be [M, %d] of %s" % (self.in_features, self.in_dtype))
+        M = x.shape[0]
+        if out is None:
+            out = torch.empty((M, self.out_features), dtype=self.out_dtype, device=x.device)
+        elif tuple(out.shape) != (M, self.out_features) or out.dtype != self.out_dtype:
+            raise ValueError("out must be [M, %d] of %s" % (self.out_features, self.out_dtype))
+        tp_proj_fwd(self.handle, x, M, out, stream)
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if getattr(self, "handle", None):
+            tp_proj_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -45,10 +45,6 @@ struct StreamShape {
   static constexpr int depth = FIRST ? 4 : 2;
 };
 
-template <int EPI>
-constexpr bool is_first() {
-  return EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
-}
 
 // Epilogue of one 32 x 32 output block whose fp32 sums sit in LDS `v` in MFMA
 // accumulator order (v[r][lane] = D[mfma32_row(r, lane)][lane % 32]).
@@ -56,7 +52,7 @@ template <int EPI, int NT>
 __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (*hb)[40], int tid,
                                                 int tile, int cb, int M, void *out, int64_t ldo,
                                                 int n_store, int ks_out) {
-  if constexpr (is_first<EPI>()) {
+  if constexpr (writes_hidden(EPI)) {
     for (int e = tid; e < 1024; e += NT) {
       const int r = e >> 6, l = e & 63, c = l & 31;
       const int R = mfma32_row(r, l);
@@ -85,7 +81,7 @@ __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (
       const int col = 32 * cb + (l & 31);
       if (row < M && col < n_store) {
         const int64_t o = static_cast<int64_t>(row) * ldo + col;
-        if constexpr (EPI == EPI_OUT_F32) static_cast<float *>(out)[o] = v[r][l];
+        if constexpr (stores_f32(EPI)) static_cast<float *>(out)[o] = v[r][l];
         else static_cast<uint16_t *>(out)[o] = f32_to_bf16(v[r][l]);
       }
     }
@@ -104,7 +100,7 @@ __global__ void __launch_bounds__((StreamShape<MT, C>::waves * 64))
 k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
          const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
          int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters) {
-  constexpr bool FIRST = is_first<EPI>();
+  constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
   constexpr int NW = StreamShape<MT, C>::waves;
   constexpr int D = StreamShape<MT, C>::template depth<FIRST>;
   constexpr int PB = D / 2;  // k-step pairs per batch
@@ -378,6 +374,10 @@ hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, in
       return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
     case EPI_OUT_BF16:
       return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_PROJ_F32:
+      return launch_epi<EPI_PROJ_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+    case EPI_PROJ_BF16:
+      return launch_epi<EPI_PROJ_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
     default:
       return hipErrorInvalidValue;
   }

@@ -82,7 +82,8 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
         void *__restrict__ out, int64_t ldo, int n_store, int ks_out, int n_whole,
         uint64_t *__restrict__ split_buf, int *__restrict__ split_cnt) {
-  constexpr bool FIRST = EPI == EPI_SILU_GATE || EPI == EPI_TANH || EPI == EPI_IDENTITY;
+  constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
+  constexpr bool HIDDEN = writes_hidden(EPI);     // epilogue writes the packed hidden buffer
   using Sh = TiledShape<SP, NW, RING>;
   static_assert(!FIRST || SP == 2, "row-major token stages are 128-byte row segments");
   constexpr int R = Sh::R, CH = Sh::CH, PW = Sh::PW, WNB = Sh::WNB, NF = Sh::NF;
@@ -328,7 +329,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   }
 
   // Epilogue.
-  if constexpr (FIRST) {
+  if constexpr (HIDDEN) {
     // h of the wave's 128 rows, FP features per pass, staged through LDS (free
     // after the last barrier of the main loop), then written as 16-byte chunks
     // of the packed hidden buffer.
@@ -384,7 +385,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         for (int j = 0; j < WNB; ++j) {
           const int col = (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
           const int64_t o = static_cast<int64_t>(row) * ldo + col;
-          if constexpr (EPI == EPI_OUT_F32) {
+          if constexpr (stores_f32(EPI)) {
             if (col < n_store) static_cast<float *>(out)[o] = acc[i][j][r];
           } else {
             if (col < n_store) static_cast<uint16_t *>(out)[o] = f32_to_bf16(acc[i][j][r]);
@@ -445,6 +446,10 @@ hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int
       return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     case EPI_OUT_BF16:
       return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+    case EPI_PROJ_F32:
+      return launch_tiled_one<EPI_PROJ_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+    case EPI_PROJ_BF16:
+      return launch_tiled_one<EPI_PROJ_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
     default:
       return hipErrorInvalidValue;
   }

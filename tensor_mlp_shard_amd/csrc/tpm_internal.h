@@ -16,7 +16,24 @@ enum Epi : int {
   EPI_IDENTITY = 2,   // h = s
   EPI_OUT_F32 = 3,    // partial stored as fp32
   EPI_OUT_BF16 = 4,   // partial stored as bf16
+  // A single projection Y = X W: row-major tokens in (as the first product),
+  // row-major Y out (as the partial store)
+  EPI_PROJ_F32 = 5,
+  EPI_PROJ_BF16 = 6,
 };
+
+// Token operand of a product: row-major X (first product, single projections) or
+// the packed hidden buffer (second product).
+constexpr bool tokens_row_major(int epi) {
+  return epi == EPI_SILU_GATE || epi == EPI_TANH || epi == EPI_IDENTITY || epi == EPI_PROJ_F32 ||
+         epi == EPI_PROJ_BF16;
+}
+// Output: the packed hidden buffer (first product) or row-major rows.
+constexpr bool writes_hidden(int epi) {
+  return epi == EPI_SILU_GATE || epi == EPI_TANH || epi == EPI_IDENTITY;
+}
+// Row-major output stored as fp32 (else bf16).
+constexpr bool stores_f32(int epi) { return epi == EPI_OUT_F32 || epi == EPI_PROJ_F32; }
 
 // ---------------------------------------------------------------------------
 // Operand layout on the matrix cores ("fragment order").

@@ -154,6 +154,50 @@ class ModelSpec:
         return [p[0] for p in pairs], [p[1] for p in pairs]
 
 
+# --------------------------------------------------------------------------
+# Attention-block projections of the same 70B-class model (page "7.4 推理侧并行",
+# section 7.4.1: 64 query heads of width 128 over d_model 8192, 8 KV heads with
+# GQA).  Each head's Q, K, V columns and Wo rows are drawn from their own seed, so
+# a rank shard at any degree dividing 8 slices one model: rank r of tp holds query
+# heads [r 64/tp, (r+1) 64/tp) and KV heads [r 8/tp, (r+1) 8/tp).
+# --------------------------------------------------------------------------
+_SEED_Q, _SEED_K, _SEED_V, _SEED_O = 4000, 5000, 6000, 7000
+
+
+@dataclass(frozen=True)
+class AttentionSpec:
+    d_model: int = D_MODEL
+    q_heads: int = 64
+    kv_heads: int = 8
+    head_dim: int = 128
+    std: float = WEIGHT_STD
+    dtype: torch.dtype = torch.bfloat16
+
+    def _head(self, base: int, h: int, rows_are_heads: bool) -> torch.Tensor:
+        shape = (self.head_dim, self.d_model) if rows_are_heads else (self.d_model, self.head_dim)
+        return randn(shape, seed=base + h, std=self.std, dtype=self.dtype)
+
+    def shard(self, rank: int, tp: int):
+        """(W_qkv [d, (q + 2 kv) head_dim], W_o [q head_dim, d]) of rank ``rank`` at
+        degree ``tp``: the rank's query-head columns, then its K and its V columns; and
+        the rows of the output projection that meet its query heads."""
+        if tp < 1 or self.q_heads % tp or self.kv_heads % tp:
+            raise ValueError("tensor-parallel degree %d must divide the head counts" % tp)
+        if not 0 <= rank < tp:
+            raise IndexError(rank)
+        qh = range(rank * self.q_heads // tp, (rank + 1) * self.q_heads // tp)
+        kh = range(rank * self.kv_heads // tp, (rank + 1) * self.kv_heads // tp)
+        cols = ([self._head(_SEED_Q, h, False) for h in qh] +
+                [self._head(_SEED_K, h, False) for h in kh] +
+                [self._head(_SEED_V, h, False) for h in kh])
+        w_qkv = torch.cat(cols, dim=1).contiguous()
+        w_o = torch.cat([self._head(_SEED_O, h, True) for h in qh], dim=0).contiguous()
+        return w_qkv, w_o
+
+    def q_width(self, tp: int) -> int:
+        return self.q_heads // tp * self.head_dim
+
+
 def tokens(M: int, d: int = D_MODEL, std: float = TOKEN_STD, dtype=torch.bfloat16,
            seed: int | None = None) -> torch.Tensor:
     """Token activations X [M, d], N(0, std^2); the seed defaults to one per M."""

@@ -202,3 +202,28 @@ def test_fp8_validation(lib):
     assert rf(qs, _ptrs(0x3000, None), 2, 4, 64, out, 0, None) == INVALID
     assert rf(_ptrs(0x1000, 0x2001), ss, 2, 4, 64, out, 0, None) == ALIGN
     assert rf(qs, ss, 2, 0, 64, out, 0, None) == OK
+
+
+def test_proj_validation(lib):
+    def rc(**kw):
+        base = dict(in_features=8192, out_features=1280, max_tokens=64, in_dtype=tpm.BF16,
+                    out_dtype=tpm.F32, path=0)
+        base.update(kw)
+        d = tpm.TpmProjDesc(base["in_features"], base["out_features"], base["max_tokens"],
+                            base["in_dtype"], base["out_dtype"], base["path"], 0)
+        h = ctypes.c_void_p()
+        return lib.tp_proj_create(ctypes.byref(d), ctypes.c_void_p(0x1000), None, ctypes.byref(h)), h
+    for kw, code in [({"in_dtype": 5}, INVALID), ({"out_dtype": 5}, INVALID), ({"path": 3}, INVALID),
+                     ({"in_features": 0}, SHAPE), ({"out_features": 0}, SHAPE),
+                     ({"max_tokens": -1}, SHAPE), ({"in_features": 100}, SHAPE),
+                     ({"in_features": 1 << 21}, SHAPE)]:
+        r, h = rc(**kw)
+        assert r == code, kw
+        assert not h.value
+    d = tpm.TpmProjDesc(64, 64, 8, tpm.BF16, tpm.F32, 0, 0)
+    h = ctypes.c_void_p()
+    assert lib.tp_proj_create(ctypes.byref(d), None, None, ctypes.byref(h)) == INVALID
+    assert lib.tp_proj_create(ctypes.byref(d), ctypes.c_void_p(0x1001), None, ctypes.byref(h)) == ALIGN
+    assert lib.tp_proj_create(None, ctypes.c_void_p(0x1000), None, ctypes.byref(h)) == INVALID
+    assert lib.tp_proj_fwd(None, None, 0, None, None) == INVALID
+    assert lib.tp_proj_destroy(None) == OK

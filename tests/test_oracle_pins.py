@@ -515,3 +515,53 @@ def test_reduce_fp8_is_sum_of_dequantized():
     bound = sum(np.abs(oracle._f64(p)) * 2.0 ** -4 + 2.0 ** -10 * s[:, None].astype(np.float64)
                 for p, (_, s) in zip(parts, qs))
     assert np.all(np.abs(z - exact) <= bound)
+
+
+# ------------------------------------------------------------ single projections
+# oracle.projection (page "大模型推理系统揭秘（07）Multi-GPU", sections 1.2.2 and
+# 1.2.4: Y = XW; QKV column-parallel, output projection row-parallel).
+
+def test_projection_brute_force_tiny():
+    X = _rand((3, 5), 1)
+    W = _rand((5, 4), 2)
+    Y = oracle.projection(X, W)
+    for i in range(3):
+        for j in range(4):
+            assert Y[i, j] == pytest.approx(math.fsum(float(X[i, k]) * float(W[k, j])
+                                                      for k in range(5)), rel=1e-14, abs=1e-15)
+
+
+def test_projection_chain_matches_mlp_identity():
+    # two projections in a row = the MLP with the identity activation (C oracle)
+    X, A, B = _rand((4, 16), 3), _rand((16, 24), 4), _rand((24, 16), 5)
+    np.testing.assert_allclose(oracle.projection(oracle.projection(X, A), B),
+                               oracle.shard_forward(X, A, B, "identity"), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_tp_identity_with_a_per_head_core():
+    """Column shards of W_qkv, a core that acts within each head, row shards of W_o:
+    the rank partials sum to the unsplit block (the column -> row identity of
+    section 1.2.3 applied to attention, section 1.2.4).  The core here is a
+    stand-in that keeps heads separate: tanh of each query head's values."""
+    spec = synth.AttentionSpec(d_model=64, q_heads=8, kv_heads=4, head_dim=8,
+                               dtype=torch.float32, std=0.2)
+    X = _rand((5, 64), 6)
+    full_q = []
+    parts = []
+    for r in range(4):
+        wqkv, wo = spec.shard(r, 4)
+        y = oracle.projection(X, wqkv)
+        a = np.tanh(y[:, :spec.q_width(4)])
+        parts.append(oracle.projection(a, wo))
+        full_q.append((wqkv[:, :spec.q_width(4)], wo))
+    Wq = np.concatenate([oracle._f64(q) for q, _ in full_q], axis=1)
+    Wo = np.concatenate([oracle._f64(o) for _, o in full_q], axis=0)
+    want = oracle.projection(np.tanh(oracle.projection(X, Wq)), Wo)
+    np.testing.assert_allclose(oracle.partials_sum(parts), want, rtol=1e-12, atol=1e-12)
+    # the shards slice one model: degree 2 gives the same block
+    parts2 = []
+    for r in range(2):
+        wqkv, wo = spec.shard(r, 2)
+        a = np.tanh(oracle.projection(X, wqkv)[:, :spec.q_width(2)])
+        parts2.append(oracle.projection(a, wo))
+    np.testing.assert_allclose(oracle.partials_sum(parts2), want, rtol=1e-12, atol=1e-12)
