@@ -25,6 +25,7 @@ The JSON line also carries
 * ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
 * ``attention_projections``: the attention block's column-parallel QKV and
   row-parallel output projections of the same model (decode and prefill shapes);
+* ``grouped_experts``: the 16 experts of one GPU as one grouped SwiGLU MLP;
 * ``reduce_add_rmsnorm``: the partials sum fused with the residual add and RMSNorm
   that follow it, against the same work in two launches;
 * ``fp8_partials``: the decode partials quantized to FP8 with per-row scales and
@@ -434,6 +435,66 @@ def run_attention_projections(tpm, lib, synth, dev):
     return res
 
 
+def run_grouped_experts(tpm, lib, synth, dev):
+    """The 16 experts of one GPU (64 experts, top-2, EP = 4) as one grouped SwiGLU MLP
+    (tp_moe_fwd: two launches for all experts) at d_model 8192, expert width 2048,
+    with seeded token counts around the page's 64-128 per expert; against one
+    tp_mlp_shard_fwd per expert (32 launches).  HIP-graph replays."""
+    import torch
+    spec = synth.ExpertSpec()
+    counts = synth.expert_counts(spec.n_experts)
+    T = sum(counts)
+    w1, w2 = spec.weights()
+    w1d, w2d = w1.to(dev), w2.to(dev)
+    del w1, w2
+    x = synth.tokens(T).to(dev)
+    y = torch.empty(T, D_MODEL, device=dev)
+    c = torch.tensor(counts, dtype=torch.int32, device=dev)
+    ge = tpm.GroupedExperts(w1d, w2d, "silu_gate", max_tokens=T)
+    vp = ctypes.c_void_p
+
+    def grouped(sp):
+        rc = lib.tp_moe_fwd(vp(ge.handle), vp(x.data_ptr()), vp(c.data_ptr()), T,
+                            vp(y.data_ptr()), sp)
+        if rc:
+            raise RuntimeError("tp_moe_fwd failed: %d" % rc)
+    shards, args, off = [], [], 0
+    for e, n in enumerate(counts):
+        sh = tpm.Shard(w1d[e], w2d[e], "silu_gate", max_tokens=n)
+        shards.append(sh)
+        args.append((vp(sh.handle), vp(x[off].data_ptr()), ctypes.c_int64(n),
+                     vp(y[off].data_ptr())))
+        off += n
+
+    def per_expert(sp):
+        for a_ in args:
+            rc = lib.tp_mlp_shard_fwd(*a_, sp)
+            if rc:
+                raise RuntimeError("tp_mlp_shard_fwd failed: %d" % rc)
+    gg, gp = _graph_of(grouped), _graph_of(per_expert)
+    t_g, t_p = _time_graph(gg, 10), _time_graph(gp, 10)
+    del gg, gp
+    for sh in shards:
+        sh.close()
+    ge.close()
+    F = spec.ffn_expert
+    wbytes = spec.n_experts * (D_MODEL * 2 * F + F * D_MODEL) * 2
+    flops = 6 * T * D_MODEL * F
+    nbytes = wbytes + T * D_MODEL * 2 + T * D_MODEL * 4
+    out = {"experts": spec.n_experts, "d_model": D_MODEL, "ffn_expert": F, "tokens": T,
+           "counts": counts, "grouped_us": round(t_g * 1e6, 2),
+           "per_expert_launches_us": round(t_p * 1e6, 2),
+           "TFLOPs": round(flops / t_g / 1e12, 1), "weight_GBs": round(wbytes / t_g / 1e9, 1)}
+    out.update(_fractions(flops, nbytes, t_g))
+    log("grouped experts (16 x d 8192 x F 2048, %d tokens): grouped %.1f us, per-expert "
+        "launches %.1f us, %.1f TFLOP/s, %.1f GB/s weights, frac %.3f (%s)"
+        % (T, t_g * 1e6, t_p * 1e6, flops / t_g / 1e12, wbytes / t_g / 1e9, out["frac"],
+           out["bound"]))
+    del w1d, w2d, x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_reduce_norm(lib, dev, reps=200):
     """The step after the all-reduce: the 8 fp32 rank partials summed, the residual
     added and RMSNorm applied, in one kernel (tp_partials_reduce_add_rmsnorm), against
@@ -698,10 +759,12 @@ def main():
         log("tensor-parallel degree sweep ...")
         sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
 
-    reduce_norm = fp8 = attn = None
+    reduce_norm = fp8 = attn = moe = None
     if not args.no_sweep:
         log("attention projections ...")
         attn = run_attention_projections(tpm, lib, synth, dev)
+        log("grouped experts ...")
+        moe = run_grouped_experts(tpm, lib, synth, dev)
         log("partials sum + residual + RMSNorm ...")
         reduce_norm = run_reduce_norm(lib, dev)
         log("fp8 partials ...")
@@ -738,6 +801,7 @@ def main():
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,
         "attention_projections": attn,
+        "grouped_experts": moe,
         "reduce_add_rmsnorm": reduce_norm,
         "fp8_partials": fp8,
         "cpu_baseline": cpu,

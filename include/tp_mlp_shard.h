@@ -280,6 +280,56 @@ tpm_status tp_proj_fwd(tpm_proj_t h, const void *X_dev, int64_t M, void *Y_dev, 
 /* Free a projection handle (waits for the device first).  NULL is OK. */
 tpm_status tp_proj_destroy(tpm_proj_t h);
 
+/* Grouped expert MLP: E experts held on this GPU, each expert e the MLP
+ * act(X_e W1_e) W2_e of the tokens X_e routed to it (page "大模型推理系统揭秘（07）
+ * Multi-GPU", MoE section: Expert_e(x) = W2,e [SiLU(W1,e x) (.) (W3,e x)], the
+ * tokens of a GPU laid out contiguously by expert and all experts' products run as
+ * one grouped GEMM).  Routing, dispatch and combine (all-to-all exchanges, router
+ * weights) are the caller's.
+ *
+ *   d_model     d, a multiple of 64.
+ *   ffn_expert  F: hidden features of one expert (no multiple constraint).
+ *   n_experts   E, 1 <= E <= 1024.
+ *   max_tokens  largest T (tokens over all experts) a fwd call may pass.
+ *   act         tpm_act (SILU_GATE: W1_e holds F gate then F up columns per row).
+ *   in_dtype    TPM_BF16 (the grouped path is bf16 only); out_dtype: dtype of Y.
+ * Constraints: TPM_ERR_SHAPE / TPM_ERR_INVALID_ARG as for the shard handle. */
+typedef struct tpm_moe_desc {
+  int64_t d_model;
+  int64_t ffn_expert;
+  int64_t n_experts;
+  int64_t max_tokens;
+  int32_t act;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  int32_t reserved;
+} tpm_moe_desc;
+
+typedef struct tpm_moe *tpm_moe_t;
+
+/* Create: W1_dev holds the E first weights back to back ([E][d x 2F] for
+ * SILU_GATE, else [E][d x F]), W2_dev the E second weights ([E][F x d]), all
+ * row-major bf16.  The handle owns packed copies; waits for `stream`. */
+tpm_status tp_moe_create(const tpm_moe_desc *desc, const void *W1_dev, const void *W2_dev,
+                         void *stream, tpm_moe_t *out);
+
+/* Y_dev[rows of expert e] = act(X_e W1_e) W2_e for every expert, in two launches.
+ *
+ *   X_dev       [T x d] bf16: the tokens of expert 0, then those of expert 1, ...
+ *   counts_dev  device array of E int32: tokens per expert, in expert order.  Read
+ *               on the device (no host synchronization); counts past the T rows
+ *               are clamped (rows of X beyond T are never read), negative counts
+ *               count as 0, and rows beyond the sum of the counts are left as they
+ *               were.
+ *   T           rows of X and Y, 0 <= T <= max_tokens (0 is a no-op).
+ *   Y_dev       [T x d] of out_dtype.
+ * Asynchronous on `stream`, allocates nothing; one handle on one stream at a time. */
+tpm_status tp_moe_fwd(tpm_moe_t h, const void *X_dev, const int32_t *counts_dev, int64_t T,
+                      void *Y_dev, void *stream);
+
+/* Free a grouped-expert handle (waits for the device first).  NULL is OK. */
+tpm_status tp_moe_destroy(tpm_moe_t h);
+
 /* Timing hook for profiling.  When `events` is non-NULL, every later fwd call on
  * this handle attaches events[2j] and events[2j+1] to its j-th kernel launch, for
  * j < kernels_per_fwd: they record the start and the end of that kernel's

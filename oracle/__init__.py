@@ -18,6 +18,8 @@ It follows the pages' statement of the method:
 * page "7.4 推理侧并行", section 7.4.2 (kernel fusion after the all-reduce): the
   residual add and RMSNorm that follow the sum (``reduce_add_rmsnorm``; RMSNorm in
   its textbook form, which the pages name without defining);
+* same page, MoE section: an expert is the SwiGLU MLP of the tokens routed to it,
+  the tokens of a GPU grouped by expert (``grouped_experts``);
 * page "大模型推理系统揭秘（07）Multi-GPU", section 1.2.4: the attention block's
   QKV projection is column-parallel and its output projection row-parallel
   (``projection``, one matrix product);
@@ -172,6 +174,23 @@ def unsplit_output(x, a_shards, b_shards, activation: str = "tanh") -> np.ndarra
     """The same MLP computed without splitting: one shard holding all hidden features."""
     A, B = unsplit_weights(a_shards, b_shards, activation)
     return shard_forward(x, A, B, activation)
+
+
+def grouped_experts(x, counts, w1s, w2s, activation: str = "silu_gate") -> np.ndarray:
+    """The experts of one GPU (page "大模型推理系统揭秘（07）Multi-GPU", MoE section):
+    rows [o_e, o_e + n_e) of x, o_e = n_0 + ... + n_{e-1}, go through expert e's MLP
+    act(x_e @ w1_e) @ w2_e; returns all rows in order, fp64."""
+    X = _f64(x)
+    out = np.zeros((X.shape[0], _f64(w2s[0]).shape[1]), dtype=np.float64)
+    off = 0
+    for n, a, b in zip(counts, w1s, w2s):
+        n = int(n)
+        if n:
+            out[off:off + n] = shard_forward(X[off:off + n], a, b, activation)
+        off += n
+    if off != X.shape[0]:
+        raise ValueError("counts sum to %d, x has %d rows" % (off, X.shape[0]))
+    return out
 
 
 def projection(x, w) -> np.ndarray:

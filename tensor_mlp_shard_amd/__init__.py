@@ -10,11 +10,13 @@ The functions carry the names of the C ABI (``include/tp_mlp_shard.h``):
   ``tp_mlp_shard_destroy``, ``tp_partials_reduce``,
   ``tp_partials_reduce_add_rmsnorm``, ``tp_partials_quantize_fp8``,
   ``tp_partials_reduce_fp8``, ``tp_proj_create``, ``tp_proj_fwd``,
-  ``tp_proj_destroy``, ``tpm_status_str``,
+  ``tp_proj_destroy``, ``tp_moe_create``, ``tp_moe_fwd``, ``tp_moe_destroy``,
+  ``tpm_status_str``,
   ``tp_mlp_shard_set_timing_events``;
 
 plus conveniences: ``Shard`` (one rank's MLP handle), ``Projection`` (one rank's
-shard of a single projection, e.g. the attention QKV or output projection) and
+shard of a single projection, e.g. the attention QKV or output projection),
+``GroupedExperts`` (the experts of one GPU as a grouped MLP) and
 ``tensor_parallel_output(x, a_shards, b_shards, activation="tanh")``, the pages'
 statement Z = sum_i act(x @ a_i) @ b_i (page "LLM 推理并行化：先找瓶颈，再决定怎么
 切", section 三.2), which raises ``ValueError`` when the shard lists differ in length.
@@ -28,7 +30,8 @@ __all__ = [
     "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
     "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tp_partials_quantize_fp8",
     "tp_partials_reduce_fp8", "tp_proj_create", "tp_proj_fwd", "tp_proj_destroy",
-    "Projection", "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
+    "Projection", "tp_moe_create", "tp_moe_fwd", "tp_moe_destroy", "GroupedExperts",
+    "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
     "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
 ]
 
@@ -60,6 +63,13 @@ class TpmProjDesc(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
+
+
+class TpmMoeDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int64), ("ffn_expert", ctypes.c_int64),
+                ("n_experts", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
+                ("act", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class TpmError(RuntimeError):
@@ -106,6 +116,12 @@ def capi():
     lib.tp_proj_fwd.restype = ctypes.c_int
     lib.tp_proj_destroy.argtypes = [vp]
     lib.tp_proj_destroy.restype = ctypes.c_int
+    lib.tp_moe_create.argtypes = [ctypes.POINTER(TpmMoeDesc), vp, vp, vp, ctypes.POINTER(vp)]
+    lib.tp_moe_create.restype = ctypes.c_int
+    lib.tp_moe_fwd.argtypes = [vp, vp, vp, i64, vp, vp]
+    lib.tp_moe_fwd.restype = ctypes.c_int
+    lib.tp_moe_destroy.argtypes = [vp]
+    lib.tp_moe_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_destroy.argtypes = [vp]
     lib.tp_mlp_shard_destroy.restype = ctypes.c_int
     lib.tp_mlp_shard_set_timing_events.argtypes = [vp, ctypes.POINTER(vp), i32]
@@ -389,6 +405,66 @@ class Projection:
     def close(self):
         if getattr(self, "handle", None):
             tp_proj_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tp_moe_create(desc: TpmMoeDesc, W1, W2, stream=None) -> int:
+    h = ctypes.c_void_p()
+    _check(capi().tp_moe_create(ctypes.byref(desc), _dev_ptr(W1, "W1"), _dev_ptr(W2, "W2"),
+                                _stream_ptr(stream), ctypes.byref(h)), "tp_moe_create")
+    return h.value
+
+
+def tp_moe_fwd(handle: int, X, counts, T: int, Y, stream=None) -> None:
+    _check(capi().tp_moe_fwd(ctypes.c_void_p(handle), _dev_ptr(X, "X"), _dev_ptr(counts, "counts"),
+                             int(T), _dev_ptr(Y, "Y"), _stream_ptr(stream)), "tp_moe_fwd")
+
+
+def tp_moe_destroy(handle: int) -> None:
+    _check(capi().tp_moe_destroy(ctypes.c_void_p(handle)), "tp_moe_destroy")
+
+
+class GroupedExperts:
+    """The experts held by one GPU as one grouped MLP.  w1: [E, d, 2F] (silu_gate:
+    gate then up columns) or [E, d, F]; w2: [E, F, d]; bf16 on the GPU."""
+
+    def __init__(self, w1, w2, activation="silu_gate", max_tokens=8192, out_dtype=None,
+                 stream=None):
+        torch = _torch()
+        if w1.dim() != 3 or w2.dim() != 3 or w1.shape[0] != w2.shape[0]:
+            raise ValueError("w1 [E, d, n1] and w2 [E, F, d] with the same E")
+        E, d, F = w1.shape[0], w1.shape[1], w2.shape[1]
+        if w1.shape[2] != (2 * F if activation == "silu_gate" else F) or w2.shape[2] != d:
+            raise ValueError("expert weight shapes do not fit activation %s" % activation)
+        self.n_experts, self.d_model, self.ffn_expert = E, d, F
+        self.out_dtype = out_dtype if out_dtype is not None else torch.float32
+        self.max_tokens = int(max_tokens)
+        self.desc = TpmMoeDesc(d, F, E, self.max_tokens, ACT[activation], _dtype_code(w1.dtype),
+                               _dtype_code(self.out_dtype), 0)
+        self.handle = tp_moe_create(self.desc, w1, w2, stream)
+
+    def forward(self, x, counts, out=None, stream=None):
+        """x: [T, d] tokens grouped by expert; counts: int32 [E] on the GPU."""
+        torch = _torch()
+        T = x.shape[0]
+        if counts.dtype != torch.int32 or counts.numel() != self.n_experts:
+            raise ValueError("counts must be int32 [%d]" % self.n_experts)
+        if out is None:
+            out = torch.empty((T, self.d_model), dtype=self.out_dtype, device=x.device)
+        tp_moe_fwd(self.handle, x, counts, T, out, stream)
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if getattr(self, "handle", None):
+            tp_moe_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

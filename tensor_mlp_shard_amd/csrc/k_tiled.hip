@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
         void *__restrict__ out, int64_t ldo, int n_store, int ks_out, int n_whole,
-        uint64_t *__restrict__ split_buf, int *__restrict__ split_cnt) {
+        uint64_t *__restrict__ split_buf, int *__restrict__ split_cnt, TiledGroups grp) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
   constexpr bool HIDDEN = writes_hidden(EPI);     // epilogue writes the packed hidden buffer
   using Sh = TiledShape<SP, NW, RING>;
@@ -119,12 +119,42 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   }
   const int k_lo = split && khalf ? k_total / 2 : 0;
   const int k_tiles = split && !khalf ? k_total / 2 : k_total - k_lo;
-  // Tile coordinates: grouped by kGroupRows tile rows.
-  const int per_group = kGroupRows * ntn;
-  const int first_m = (t / per_group) * kGroupRows;
-  const int gm = min(ntm - first_m, kGroupRows);
-  const int tm = first_m + (t % per_group) % gm;
-  const int tn = (t % per_group) / gm;
+  // Tile coordinates.  row0: first token row of the tile (X rows / output rows),
+  // row_end: end of the valid rows, hrow0: first row in the packed hidden buffer,
+  // Wt: the weight the tile multiplies.
+  int tn, row0, row_end, hrow0;
+  const u32x4_t *Wt = W;
+  if (grp.n_groups == 0) {
+    // one matrix: tiles grouped by kGroupRows tile rows
+    const int per_group = kGroupRows * ntn;
+    const int first_m = (t / per_group) * kGroupRows;
+    const int gm = min(ntm - first_m, kGroupRows);
+    const int tm = first_m + (t % per_group) % gm;
+    tn = (t % per_group) / gm;
+    row0 = hrow0 = tm * kTileM;
+    row_end = M;
+  } else {
+    // grouped (one weight per group, the groups' rows contiguous in X): tile row
+    // t / ntn counts through the groups' row tiles in group order; each group's
+    // hidden rows start on a tile boundary.  Group sizes come from device memory and
+    // are clamped to the M rows there are; a workgroup past the last tile exits.
+    int rt = t / ntn;
+    tn = t % ntn;
+    int off = 0, hoff = 0, g = 0, n = 0;
+    for (; g < grp.n_groups; ++g) {
+      n = min(max(grp.counts[g], 0), M - off);
+      const int tiles = (n + kTileM - 1) / kTileM;
+      if (rt < tiles) break;
+      rt -= tiles;
+      off += n;
+      hoff += tiles * kTileM;
+    }
+    if (g == grp.n_groups) return;  // uniform over the workgroup: no tile left
+    row0 = off + rt * kTileM;
+    row_end = off + n;
+    hrow0 = hoff + rt * kTileM;
+    Wt = W + static_cast<int64_t>(g) * grp.w_stride;
+  }
 
   // Stage layout: chunk c < 16 SP is token fragment (row block (c / 2) % 8, k-step
   // 2 (c / 16) + c % 2 of the stage) for the packed hidden buffer, or 8 whole token
@@ -149,18 +179,18 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         // cache lines, and the swizzle keeps the fragment reads free of bank
         // conflicts.
         const int r = 8 * c + (lane >> 3);
-        int row = tm * kTileM + r;
-        row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
+        int row = row0 + r;
+        row = row < row_end ? row : row_end - 1;  // rows past the end repeat the last; never stored
         const int piece = (lane & 7) ^ tok_swz(r);
         src[q] = reinterpret_cast<const u32x4_t *>(A + static_cast<int64_t>(row) * lda + 8 * piece);
         step[q] = 4 * SP;  // 32 SP bf16
       } else {
         src[q] = reinterpret_cast<const u32x4_t *>(A) +
-                 ((static_cast<int64_t>(tm) * 8 + blk) * k_blocks + kstep) * 64 + lane;
+                 ((static_cast<int64_t>(hrow0 >> 5) + blk) * k_blocks + kstep) * 64 + lane;
         step[q] = 2 * SP * 64;
       }
     } else {
-      src[q] = W + (static_cast<int64_t>(kstep) * ntn * 8 + tn * 8 + blk) * 64 + lane;
+      src[q] = Wt + (static_cast<int64_t>(kstep) * ntn * 8 + tn * 8 + blk) * 64 + lane;
       step[q] = static_cast<int64_t>(2 * SP) * ntn * 8 * 64;
     }
     src[q] += step[q] * k_lo;  // first stage of this workgroup's contraction range
@@ -367,7 +397,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         const int R_ = q & 127, qc = q >> 7;
         const int jf = f0 + 8 * qc;
         const int s = 2 * (jf >> 5) + ((jf >> 3) & 1);
-        const int row = tm * kTileM + wm * 128 + R_;
+        const int row = hrow0 + wm * 128 + R_;
         const int ln = 32 * ((jf >> 4) & 1) + (row & 31);
         const int64_t chunk = (static_cast<int64_t>(row >> 5) * ks_out + s) * 64 + ln;
         static_cast<u32x4_t *>(out)[chunk] = *reinterpret_cast<const u32x4_t *>(&hs[R_ * HS + 8 * qc]);
@@ -379,8 +409,8 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = tm * kTileM + (wm * 4 + i) * 32 + mfma32_row(r, lane);
-        if (row >= M) continue;
+        const int row = row0 + (wm * 4 + i) * 32 + mfma32_row(r, lane);
+        if (row >= row_end) continue;
 #pragma unroll
         for (int j = 0; j < WNB; ++j) {
           const int col = (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
@@ -412,13 +442,14 @@ int tiled_split_tiles(int64_t tiles, int n_cu, int max_tiles) {
 template <int EPI, int SP = kTiledSP, int NW = kTiledWaves, int RING = kTiledRing>
 static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
                                    int64_t n_packed, void *out, int64_t ldo, int64_t n_store,
-                                   int64_t ks_out, const TiledSplit &sp, hipStream_t s,
-                                   const Timing &t) {
-  const int ntm = static_cast<int>((M + kTileM - 1) / kTileM);
+                                   int64_t ks_out, const TiledSplit &sp, const TiledGroups &grp,
+                                   hipStream_t s, const Timing &t) {
+  // grouped: every group may add one partial row tile
+  const int ntm = static_cast<int>((M + kTileM - 1) / kTileM) + grp.n_groups;
   const int ntn = static_cast<int>(n_packed / kTileN);
   if (K % (32 * SP)) return hipErrorInvalidValue;
   const int k_total = static_cast<int>(K / (32 * SP));
-  const int split = (sp.buf && sp.cnt && k_total >= 2 * RING)
+  const int split = (grp.n_groups == 0 && sp.buf && sp.cnt && k_total >= 2 * RING)
                         ? tiled_split_tiles(static_cast<int64_t>(ntm) * ntn, sp.n_cu, sp.max_tiles)
                         : 0;
   const int n_whole = ntm * ntn - split;
@@ -427,29 +458,29 @@ static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_
                         static_cast<int>(M), k_total, static_cast<const u32x4_t *>(W),
                         static_cast<int>(K / kFragK), ntm, ntn, out, ldo,
                         static_cast<int>(n_store), static_cast<int>(ks_out), n_whole,
-                        static_cast<uint64_t *>(sp.buf), sp.cnt);
+                        static_cast<uint64_t *>(sp.buf), sp.cnt, grp);
   return hipGetLastError();
 }
 
 hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K,
                              const void *W, int64_t n_packed, void *out, int64_t ldo,
                              int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
-                             const Timing &t) {
+                             const Timing &t, const TiledGroups &grp) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_SILU_GATE>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_TANH:
-      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_TANH>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_IDENTITY:
-      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_IDENTITY>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_OUT_F32:
-      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_OUT_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_OUT_BF16:
-      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_OUT_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_PROJ_F32:
-      return launch_tiled_one<EPI_PROJ_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_PROJ_F32>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     case EPI_PROJ_BF16:
-      return launch_tiled_one<EPI_PROJ_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
+      return launch_tiled_one<EPI_PROJ_BF16>(A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, grp, s, t);
     default:
       return hipErrorInvalidValue;
   }

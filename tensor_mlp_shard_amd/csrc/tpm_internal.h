@@ -170,11 +170,23 @@ struct TiledSplit {
 // max_tiles) that run as two contraction halves.
 int tiled_split_tiles(int64_t tiles, int n_cu, int max_tiles);
 
+// Grouped tiled product: n_groups weights, packed back to back (w_stride 16-byte
+// chunks apart), each applied to its own contiguous run of token rows whose
+// lengths sit in device memory (counts[g]; the runs are taken in group order and
+// clamped to the M rows there are).  Hidden rows of a group start on a 256-row
+// boundary: the hidden buffer needs round_up(M, 256) + 256 n_groups rows.
+// n_groups = 0: a single matrix.
+struct TiledGroups {
+  const int *counts = nullptr;
+  int n_groups = 0;
+  int64_t w_stride = 0;
+};
+
 // Prefill-path products, same operand and output conventions as above.
 hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K,
                              const void *W, int64_t n_packed, void *out, int64_t ldo,
                              int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
-                             const Timing &t = Timing());
+                             const Timing &t = Timing(), const TiledGroups &grp = TiledGroups());
 
 hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int64_t K,
                            const float *B, int64_t ldb, int64_t N, int64_t up_offset, void *out,

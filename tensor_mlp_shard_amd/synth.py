@@ -198,6 +198,42 @@ class AttentionSpec:
         return self.q_heads // tp * self.head_dim
 
 
+# --------------------------------------------------------------------------
+# Experts of one GPU for the grouped expert MLP (page "大模型推理系统揭秘（07）
+# Multi-GPU", MoE section: 64 experts with top-2 routing over EP = 4 GPUs, so 16
+# experts per GPU; its grouped-GEMM example gives one GPU's experts 128, 64 and 96
+# tokens).  The expert width is not given there; 2048 is used.  Each expert's
+# weights come from their own seeds; token counts per expert are drawn around the
+# example's 64-128.
+# --------------------------------------------------------------------------
+_SEED_EXPERT = 9000
+
+
+@dataclass(frozen=True)
+class ExpertSpec:
+    d_model: int = D_MODEL
+    ffn_expert: int = 2048
+    n_experts: int = 16
+    std: float = WEIGHT_STD
+    dtype: torch.dtype = torch.bfloat16
+
+    def weights(self, activation: str = "silu_gate"):
+        """(W1 [E, d, 2F or F], W2 [E, F, d]) of the GPU's experts."""
+        cols = 2 * self.ffn_expert if activation == "silu_gate" else self.ffn_expert
+        w1 = torch.stack([randn((self.d_model, cols), _SEED_EXPERT + 2 * e, self.std, self.dtype)
+                          for e in range(self.n_experts)])
+        w2 = torch.stack([randn((self.ffn_expert, self.d_model), _SEED_EXPERT + 2 * e + 1,
+                                self.std, self.dtype) for e in range(self.n_experts)])
+        return w1, w2
+
+
+def expert_counts(n_experts: int, lo: int = 64, hi: int = 128, seed: int = 77) -> list[int]:
+    """Tokens per expert, uniform on [lo, hi], seeded."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randint(lo, hi + 1, (n_experts,), generator=g).tolist()
+
+
 def tokens(M: int, d: int = D_MODEL, std: float = TOKEN_STD, dtype=torch.bfloat16,
            seed: int | None = None) -> torch.Tensor:
     """Token activations X [M, d], N(0, std^2); the seed defaults to one per M."""

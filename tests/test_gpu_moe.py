@@ -1,0 +1,110 @@
+"""GPU parity of the grouped expert MLP (tp_moe_*) against the fp64 oracle, through
+the C ABI: the page's example counts, random counts with empty and ragged groups,
+counts that overrun the token rows (clamped), and determinism.  Bound: 2e-2
+(bf16 inputs, fp32 accumulation), max-abs over RMS."""
+import ctypes
+
+import pytest
+import torch
+
+import oracle
+import tensor_mlp_shard_amd as tpm
+from tensor_mlp_shard_amd import synth
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+TOL_BF16 = 2e-2
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run(spec, counts, T=None, act="silu_gate", out_dtype=torch.float32, seed=5, reps=1):
+    w1, w2 = spec.weights(act)
+    T = sum(counts) if T is None else T
+    x = synth.tokens(T, d=spec.d_model, seed=seed)
+    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), act, max_tokens=max(T, 1), out_dtype=out_dtype)
+    try:
+        c = torch.tensor(counts, dtype=torch.int32, device=DEV)
+        outs = []
+        for _ in range(reps):
+            y = torch.full((T, spec.d_model), 7.0, device=DEV).to(out_dtype)
+            ge.forward(x.to(DEV), c, out=y)
+            torch.cuda.synchronize()
+            outs.append(y.cpu())
+        return x, w1, w2, outs
+    finally:
+        ge.close()
+
+
+def check(x, counts, w1, w2, y, act="silu_gate", rows=None):
+    n = min(sum(max(c, 0) for c in counts), x.shape[0])
+    eff, left = [], n
+    for c in counts:
+        k = min(max(c, 0), left)
+        eff.append(k)
+        left -= k
+    if rows is None:
+        ref = oracle.grouped_experts(x[:n], eff, list(w1), list(w2), act)
+        got = y[:n]
+    else:
+        # only the sampled rows: each through its own expert
+        rows = sorted(r for r in rows if r < n)
+        sub_counts, off, e_rows = [], 0, []
+        for c in eff:
+            mine = [r for r in rows if off <= r < off + c]
+            sub_counts.append(len(mine))
+            e_rows += mine
+            off += c
+        ref = oracle.grouped_experts(x[e_rows], sub_counts, list(w1), list(w2), act)
+        got = y[e_rows]
+    err = oracle.rel_err(got, ref)
+    say("experts err", err)
+    assert err <= TOL_BF16
+
+
+def test_page_example_counts():
+    spec = synth.ExpertSpec(d_model=1024, ffn_expert=512, n_experts=3)
+    counts = [128, 64, 96]
+    x, w1, w2, (y,) = run(spec, counts)
+    check(x, counts, w1, w2, y)
+
+
+@pytest.mark.parametrize("act", ["silu_gate", "tanh", "identity"])
+def test_ragged_and_empty_groups(act):
+    spec = synth.ExpertSpec(d_model=512, ffn_expert=300, n_experts=6)
+    counts = [0, 300, 1, 255, 256, 257]
+    x, w1, w2, (y,) = run(spec, counts, act=act)
+    check(x, counts, w1, w2, y, act)
+
+
+def test_sixteen_experts_bf16_out_and_deterministic():
+    spec = synth.ExpertSpec(d_model=2048, ffn_expert=1024, n_experts=16)
+    counts = synth.expert_counts(16)
+    x, w1, w2, ys = run(spec, counts, out_dtype=torch.bfloat16, reps=2)
+    assert torch.equal(ys[0], ys[1])
+    check(x, counts, w1, w2, ys[0], rows=synth.sample_rows(sum(counts), 200))
+
+
+def test_counts_past_the_rows_are_clamped_and_rows_past_the_counts_untouched():
+    spec = synth.ExpertSpec(d_model=256, ffn_expert=128, n_experts=4)
+    # the counts claim 40 + 50 + 60 + 70 rows, X holds 100: experts 0, 1 and the first
+    # 10 rows of expert 2 are computed, nothing past row 100 is read or written
+    x, w1, w2, (y,) = run(spec, [40, 50, 60, 70], T=100)
+    check(x, [40, 50, 60, 70], w1, w2, y)
+    # counts summing to less than T: rows past the sum keep their old value
+    x, w1, w2, (y,) = run(spec, [10, -3, 5, 0], T=40)
+    check(x, [10, 0, 5, 0], w1, w2, y)
+    assert torch.all(y[15:] == 7.0)
+
+
+def test_full_size_expert_layer_sampled():
+    """The 16 experts of one GPU at the 70B-class width (d 8192, expert width 2048)."""
+    spec = synth.ExpertSpec()
+    counts = synth.expert_counts(spec.n_experts)
+    say("16 experts d 8192, F 2048, tokens", sum(counts))
+    x, w1, w2, (y,) = run(spec, counts)
+    check(x, counts, w1, w2, y, rows=synth.sample_rows(sum(counts), 48))

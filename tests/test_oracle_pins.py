@@ -565,3 +565,54 @@ def test_attention_tp_identity_with_a_per_head_core():
         a = np.tanh(oracle.projection(X, wqkv)[:, :spec.q_width(2)])
         parts2.append(oracle.projection(a, wo))
     np.testing.assert_allclose(oracle.partials_sum(parts2), want, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------- grouped experts
+# oracle.grouped_experts (page "大模型推理系统揭秘（07）Multi-GPU", MoE section).
+
+def _experts(E, d, F, seed):
+    spec = synth.ExpertSpec(d_model=d, ffn_expert=F, n_experts=E, dtype=torch.float32, std=0.2)
+    return spec.weights("silu_gate")
+
+
+def test_experts_single_group_is_the_mlp():
+    w1, w2 = _experts(1, 16, 12, 0)
+    X = _rand((7, 16), 21)
+    np.testing.assert_array_equal(oracle.grouped_experts(X, [7], [w1[0]], [w2[0]]),
+                                  oracle.shard_forward(X, w1[0], w2[0], "silu_gate"))
+
+
+def test_experts_page_example_counts_rowwise():
+    # the page's grouped-GEMM example: one GPU's experts receive 128, 64 and 96 tokens
+    w1, w2 = _experts(3, 16, 8, 1)
+    counts = [128, 64, 96]
+    X = _rand((sum(counts), 16), 22)
+    Y = oracle.grouped_experts(X, counts, list(w1), list(w2))
+    off = 0
+    for e, n in enumerate(counts):
+        for r in (off, off + n - 1):  # first and last row of each group, brute force
+            h = []
+            for j in range(8):
+                g = math.fsum(float(X[r, k]) * float(w1[e][k, j]) for k in range(16))
+                u = math.fsum(float(X[r, k]) * float(w1[e][k, 8 + j]) for k in range(16))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            for c in range(16):
+                want = math.fsum(h[j] * float(w2[e][j, c]) for j in range(8))
+                assert Y[r, c] == pytest.approx(want, rel=1e-12, abs=1e-13)
+        off += n
+
+
+def test_experts_permuting_groups_permutes_rows_and_empty_groups():
+    w1, w2 = _experts(4, 16, 8, 2)
+    counts = [3, 0, 5, 2]
+    X = _rand((10, 16), 23)
+    Y = oracle.grouped_experts(X, counts, list(w1), list(w2))
+    # experts in the order 2, 0, 3 (expert 1 has no tokens): rows move with their groups
+    order = [2, 0, 3]
+    offs = {0: 0, 2: 3, 3: 8}
+    rows = sum([list(range(offs[e], offs[e] + counts[e])) for e in order], [])
+    Y2 = oracle.grouped_experts(X[rows], [counts[e] for e in order], [w1[e] for e in order],
+                                [w2[e] for e in order])
+    np.testing.assert_array_equal(Y2, Y[rows])
+    with pytest.raises(ValueError):
+        oracle.grouped_experts(X, [3, 0, 5, 1], list(w1), list(w2))
