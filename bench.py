@@ -86,6 +86,33 @@ def stored_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def device_peaks(props):
+    """The published peaks the fractions use, and the dense bf16 peak that the device's
+    own CU count and maximum engine clock give (4096 bf16 flops per clock per CU)."""
+    clock_ghz = None
+    try:
+        # hipDeviceGetAttribute(hipDeviceAttributeClockRate = 5, in kHz) from the HIP runtime
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0 and v.value > 0:
+            clock_ghz = v.value / 1e6
+    except OSError:
+        pass
+    cus = props.multi_processor_count
+    out = {"cus": cus, "hbm_peak_GBs_published": HBM_PEAK_GBS,
+           "bf16_peak_TFLOPs_published": BF16_PEAK_TFLOPS}
+    if clock_ghz:
+        out["max_engine_clock_GHz"] = round(clock_ghz, 3)
+        out["bf16_peak_TFLOPs_from_clock"] = round(cus * 4096 * clock_ghz * 1e9 / 1e12, 1)
+    return out
+
+
 class Rank:
     """One rank's shard handle plus the raw C arguments of its fwd call."""
 
@@ -222,8 +249,9 @@ def run_prefill(tpm, lib, synth, dev, iters, warmup):
     lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
     k1 = [e[0].elapsed_time(e[1]) for _, e in hooks]
     k2 = [e[2].elapsed_time(e[3]) for _, e in hooks]
+    plan = {k: r.shard.plan[k] for k in ("packed_weight_bytes", "workspace_bytes")}
     r.shard.close()
-    return (t1 - t0) / iters, k1, k2
+    return (t1 - t0) / iters, k1, k2, plan
 
 
 SWEEP_TP = (1, 2, 4, 8)
@@ -686,6 +714,8 @@ def main():
     log("device:", props.name, "CUs:", props.multi_processor_count)
 
     ranks, red_args, _, host_inputs = decode_workload(tpm, lib, synth, dev)
+    handle_mem = {"decode_rank_shard": {k: ranks[0].shard.plan[k]
+                                        for k in ("packed_weight_bytes", "workspace_bytes")}}
     w_bytes_rank = D_MODEL * 2 * (FFN // TP) * 2 + (FFN // TP) * D_MODEL * 2
     w_bytes_step = TP * w_bytes_rank
     log("decode: %d steps (warmup %d), HIP-graph replay ..." % (args.steps, args.warmup))
@@ -710,11 +740,14 @@ def main():
                 "traffic": traffic,
                 "kernel": "k_stream<SILU_GATE> (gate/up projection, decode shard M=32)",
                 "algorithmic_bytes_per_launch": k1_bytes, "avg_launch_us": round(k1_ms * 1e3, 2),
-                "launches": len(k1),
+                "median_launch_us": round(_median(k1) * 1e3, 2),
+                "min_launch_us": round(min(k1) * 1e3, 2), "launches": len(k1),
                 "timing": "HIP events attached to each launch (start/end of execution), "
                           "eager pass of the same steps right after the timed replays"}
     down = {"kernel": "k_stream<OUT_F32> (down projection, decode shard M=32)",
             "algorithmic_bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2),
+            "median_launch_us": round(_median(k2) * 1e3, 2),
+            "min_launch_us": round(min(k2) * 1e3, 2),
             "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)}
     shard_us = (k1_ms + k2_ms) * 1e3
     shard_bytes = w_bytes_rank + M_DECODE * D_MODEL * 2 + M_DECODE * D_MODEL * 4
@@ -728,7 +761,8 @@ def main():
         ranks = None
         torch.cuda.empty_cache()
         log("prefill: %d iterations ..." % args.prefill_iters)
-        t_call, p1, p2 = run_prefill(tpm, lib, synth, dev, args.prefill_iters, 3)
+        t_call, p1, p2, pplan = run_prefill(tpm, lib, synth, dev, args.prefill_iters, 3)
+        handle_mem["prefill_rank_shard"] = pplan
         flops1 = 2 * M_PREFILL * D_MODEL * 2 * F
         flops2 = 2 * M_PREFILL * F * D_MODEL
         p1_ms, p2_ms = sum(p1) / len(p1), sum(p2) / len(p2)
@@ -743,6 +777,8 @@ def main():
                                 "achieved": round(flops1 / (p1_ms * 1e-3) / 1e12, 1),
                                 "frac": round(flops1 / (p1_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                                 "avg_launch_us": round(p1_ms * 1e3, 1),
+                                "median_launch_us": round(_median(p1) * 1e3, 1),
+                                "min_launch_us": round(min(p1) * 1e3, 1),
                                 "traffic": stored_traffic("gate_up_prefill")},
                    "down": {"kernel": "k_tiled<OUT_F32> (down projection)",
                             "achieved_TFLOPs": round(flops2 / (p2_ms * 1e-3) / 1e12, 1),
@@ -806,6 +842,8 @@ def main():
         "fp8_partials": fp8,
         "cpu_baseline": cpu,
         "device": props.name,
+        "device_peaks": device_peaks(props),
+        "handle_device_bytes": handle_mem,
         "source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
