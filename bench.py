@@ -686,6 +686,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-iters", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=20,
+                    help="untimed prefill calls first (the clock settles over ~10 ms of load)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
@@ -761,7 +763,8 @@ def main():
         ranks = None
         torch.cuda.empty_cache()
         log("prefill: %d iterations ..." % args.prefill_iters)
-        t_call, p1, p2, pplan = run_prefill(tpm, lib, synth, dev, args.prefill_iters, 3)
+        t_call, p1, p2, pplan = run_prefill(tpm, lib, synth, dev, args.prefill_iters,
+                                                 args.prefill_warmup)
         handle_mem["prefill_rank_shard"] = pplan
         flops1 = 2 * M_PREFILL * D_MODEL * 2 * F
         flops2 = 2 * M_PREFILL * F * D_MODEL
@@ -779,6 +782,7 @@ def main():
                                 "avg_launch_us": round(p1_ms * 1e3, 1),
                                 "median_launch_us": round(_median(p1) * 1e3, 1),
                                 "min_launch_us": round(min(p1) * 1e3, 1),
+                                "launches": len(p1), "warmup_calls": args.prefill_warmup,
                                 "traffic": stored_traffic("gate_up_prefill")},
                    "down": {"kernel": "k_tiled<OUT_F32> (down projection)",
                             "achieved_TFLOPs": round(flops2 / (p2_ms * 1e-3) / 1e12, 1),
