@@ -36,7 +36,13 @@ namespace tpm {
 // batches in flight per wave), chosen so each shape stays in registers.
 template <int MT, int C>
 struct StreamShape {
-  static constexpr int waves = (MT == 1 && C == 1) ? 16 : 8;
+  // Measured at the 70B-class decode shapes: the row-major token product streams
+  // fastest with 4 waves (one token tile, time against 4 waves: 16 waves +4%, 8 +2%,
+  // 2 +25%, deeper register pipelines of 3 or 4 batches +3%; two token tiles: 8
+  // waves up to +6%), the packed hidden product with 8 (16, whose waves then get
+  // only 14 k-steps each: +14%; 4: +6%).
+  template <bool FIRST>
+  static constexpr int waves = (FIRST && C == 1) ? 4 : 8;
   // k-steps per load batch: two pairs when the token operand is staged as 128-byte
   // row segments; one pair for the packed hidden operand, whose short contraction
   // (a few batches per wave) gains from the finer pipeline (measured: 7% on the
@@ -96,12 +102,12 @@ __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (
 // result does not depend on arrival order), runs the epilogue and resets the
 // counter to zero for the next call.  Nothing ever waits for another workgroup.
 template <int EPI, int MT, int C>
-__global__ void __launch_bounds__((StreamShape<MT, C>::waves * 64))
+__global__ void __launch_bounds__((StreamShape<MT, C>::template waves<tokens_row_major(EPI)> * 64))
 k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
          const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
          int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
-  constexpr int NW = StreamShape<MT, C>::waves;
+  constexpr int NW = StreamShape<MT, C>::template waves<FIRST>;
   constexpr int D = StreamShape<MT, C>::template depth<FIRST>;
   constexpr int PB = D / 2;  // k-step pairs per batch
   constexpr int NT = NW * 64;
@@ -316,7 +322,8 @@ hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, 
   if (n_cb % C || S < 1 || (S > 1 && (!scratch || !counters)) || blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
   hipExtLaunchKernelGGL((k_stream<EPI, MT, C>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(StreamShape<MT, C>::waves * 64), 0, s, t.start, t.stop, 0,
+                     dim3(StreamShape<MT, C>::template waves<tokens_row_major(EPI)> * 64), 0, s,
+                     t.start, t.stop, 0,
                      static_cast<const uint16_t *>(A),
                      lda, static_cast<int>(M), static_cast<int>(ks),
                      static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
