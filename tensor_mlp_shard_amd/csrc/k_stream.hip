@@ -32,17 +32,11 @@ namespace tpm {
 
 // Launch shapes.  C column blocks per workgroup: every token fragment a wave loads
 // feeds C products, so the token operand costs 1/C of the weight traffic through
-// the vector caches.  NW waves per workgroup, D k-steps per load batch (two
-// batches in flight per wave), chosen so each shape stays in registers.
+// the vector caches.  D k-steps per load batch (two batches in flight per wave),
+// chosen so each shape stays in registers.  Waves per workgroup (NW, a template
+// parameter of the kernel): see stream_waves.
 template <int MT, int C>
 struct StreamShape {
-  // Measured at the 70B-class decode shapes: the row-major token product streams
-  // fastest with 4 waves (one token tile, time against 4 waves: 16 waves +4%, 8 +2%,
-  // 2 +25%, deeper register pipelines of 3 or 4 batches +3%; two token tiles: 8
-  // waves up to +6%), the packed hidden product with 8 (16, whose waves then get
-  // only 14 k-steps each: +14%; 4: +6%).
-  template <bool FIRST>
-  static constexpr int waves = (FIRST && C == 1) ? 4 : 8;
   // k-steps per load batch: two pairs when the token operand is staged as 128-byte
   // row segments; one pair for the packed hidden operand, whose short contraction
   // (a few batches per wave) gains from the finer pipeline (measured: 7% on the
@@ -101,13 +95,12 @@ __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (
 // arrival counter; the last to arrive adds the S slices in slice order (so the
 // result does not depend on arrival order), runs the epilogue and resets the
 // counter to zero for the next call.  Nothing ever waits for another workgroup.
-template <int EPI, int MT, int C>
-__global__ void __launch_bounds__((StreamShape<MT, C>::template waves<tokens_row_major(EPI)> * 64))
+template <int EPI, int MT, int C, int NW>
+__global__ void __launch_bounds__(NW * 64)
 k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
          const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
          int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
-  constexpr int NW = StreamShape<MT, C>::template waves<FIRST>;
   constexpr int D = StreamShape<MT, C>::template depth<FIRST>;
   constexpr int PB = D / 2;  // k-step pairs per batch
   constexpr int NT = NW * 64;
@@ -311,6 +304,28 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Waves per workgroup, measured at the 70B-class decode shapes.  A whole contraction
+// of the row-major token product streams fastest with 4 (gate/up, one token tile,
+// time against 4 waves: 16 waves +4%, 8 +2%, 2 +25%, deeper register pipelines of 3
+// or 4 batches +3%; two token tiles: 8 waves up to +6%; the 1024-deep attention
+// output shard: 8 waves +10%); its contraction slices with 8 (the 40-block QKV shard
+// in 4 slices: 4 waves +10%, 16 +2%); the packed hidden product with 8 (16, whose
+// waves then get only 14 k-steps each: +14%; 4: +6%).
+constexpr int stream_waves(bool first, int S) { return first && S == 1 ? 4 : 8; }
+
+template <int EPI, int MT, int C, int NW>
+hipError_t launch_stream_nw(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
+                            int64_t n_units, int64_t blocks, int S, void *out, int64_t ldo,
+                            int64_t n_store, int64_t ks_out, float *scratch, int *counters,
+                            hipStream_t s, const Timing &t) {
+  hipExtLaunchKernelGGL((k_stream<EPI, MT, C, NW>), dim3(static_cast<unsigned>(blocks)),
+                        dim3(NW * 64), 0, s, t.start, t.stop, 0, static_cast<const uint16_t *>(A),
+                        lda, static_cast<int>(M), static_cast<int>(ks),
+                        static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
+                        static_cast<int>(n_store), static_cast<int>(ks_out), scratch, counters);
+  return hipGetLastError();
+}
+
 template <int EPI, int MT, int C>
 hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
                              int64_t n_cb, int S, void *out, int64_t ldo, int64_t n_store,
@@ -321,14 +336,11 @@ hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, 
   const int64_t blocks = n_units * S * groups;
   if (n_cb % C || S < 1 || (S > 1 && (!scratch || !counters)) || blocks > 0x7fffffff)
     return hipErrorInvalidConfiguration;
-  hipExtLaunchKernelGGL((k_stream<EPI, MT, C>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(StreamShape<MT, C>::template waves<tokens_row_major(EPI)> * 64), 0, s,
-                     t.start, t.stop, 0,
-                     static_cast<const uint16_t *>(A),
-                     lda, static_cast<int>(M), static_cast<int>(ks),
-                     static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
-                     static_cast<int>(n_store), static_cast<int>(ks_out), scratch, counters);
-  return hipGetLastError();
+  if (stream_waves(tokens_row_major(EPI), S) == 4)
+    return launch_stream_nw<EPI, MT, C, 4>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
+                                           ks_out, scratch, counters, s, t);
+  return launch_stream_nw<EPI, MT, C, 8>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
+                                         ks_out, scratch, counters, s, t);
 }
 
 StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
@@ -341,10 +353,13 @@ StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
   // whenever there are enough blocks to occupy most compute units (measured at the
   // 70B-class decode shapes: wider groups or contraction slices only add traffic or
   // arrival latency there).  Narrow shards instead slice the contraction so that
-  // about 256 workgroups stream the weight.
+  // about 160 workgroups stream the weight: each slice adds its share of the
+  // hand-off through the last arriving workgroup (measured on the 40-block QKV shard
+  // of the 70B-class attention, 8 waves: 80, 120, 160, 240, 320 and 480 workgroups
+  // take 14.8, 13.0, 11.7, 12.6, 14.6 and 17.1 us).
   const int64_t wgs = n_cb * groups;
   if (wgs >= 192) return p;
-  int64_t s = 256 / wgs;
+  int64_t s = (160 + wgs / 2) / wgs;
   const int64_t max_s = (ks / 4) / 8;  // >= 8 batches of 2 pairs per slice
   if (s > max_s) s = max_s;
   if (s > kStreamMaxSlices) s = kStreamMaxSlices;
