@@ -76,7 +76,7 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds) {
 // touches land, for any 8 or 16 consecutive lanes, on distinct 16-byte bank groups.
 __device__ __forceinline__ int tok_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <int EPI, int SP, int NW, int RING>
+template <int EPI, int SP, int NW, int RING, bool PART>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
         const u32x4_t *__restrict__ W, int k_blocks, int ntm, int ntn,
@@ -164,6 +164,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   // source address is the lane's own piece of that chunk.
   const u32x4_t *src[PW];
   int64_t step[PW];  // source advance per stage, in 16-byte units
+  bool skip[PW];     // PART: token chunk wholly past the valid rows, never loaded
 #pragma unroll
   for (int q = 0; q < PW; ++q) {
     const int c = PW * wave + q;  // wave-uniform
@@ -171,6 +172,7 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
     const int cc = tok ? c : c - 16 * SP;
     const int blk = (cc >> 1) & 7;               // row or column block within the tile
     const int kstep = 2 * (cc >> 4) + (cc & 1);  // k-step within the stage
+    skip[q] = PART && tok && row0 + (FIRST ? 8 * c : 32 * blk) >= row_end;
     if (tok) {
       if constexpr (FIRST) {
         // Row-major tokens: chunk c holds tile rows 8 c .. 8 c + 7, each as its
@@ -199,12 +201,12 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   auto issue_part = [&](int kt, int buf, int part) {
 #pragma unroll
     for (int q = part * (PW / 4); q < (part + 1) * (PW / 4); ++q)
-      load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
+      if (!skip[q]) load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
   };
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int q = 0; q < PW; ++q)
-      load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
+      if (!skip[q]) load_lds16(src[q] + step[q] * kt, &lds[buf][PW * wave + q][0]);
   };
 
   f32x16_t acc[4][WNB];
@@ -241,14 +243,21 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
 #pragma unroll
     for (int q = 0; q < NF; ++q) f[q] = frag(buf, ksi, q);
   };
+  // PART (grouped launches, whose tiles often hold a short run of tokens): the row
+  // blocks of this wave's 128 rows past the valid rows (wave-uniform) skip their
+  // products and token fragment reads; their sums stay zero and are never stored as
+  // output (a hidden row past the end holds act(0) = 0).
+  const int wrows = row_end - row0 - wm * 128;
+  const int nvb = !PART ? 4 : wrows <= 0 ? 0 : min(4, (wrows + 31) >> 5);
   // Fragments q, q + 1 (if they exist) of one k-step.
   auto read_pair = [&](int buf, int ksi, u32x4_t (&f)[NF], int q) {
 #pragma unroll
     for (int r = q; r < q + 2; ++r)
-      if (r < NF) f[r] = frag(buf, ksi, r);
+      if (r < NF && (!PART || r >= 4 || r < nvb)) f[r] = frag(buf, ksi, r);
   };
   // The products of token fragment row i of one k-step.
   auto mfma_row = [&](const u32x4_t (&f)[NF], int i) {
+    if (PART && i >= nvb) return;
 #pragma unroll
     for (int j = 0; j < WNB; ++j) acc[i][j] = mfma_32x32x16(f[i], f[4 + j], acc[i][j]);
   };
@@ -258,7 +267,9 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   // LDS and nobody reads the buffer of stage kt any more.
   auto sync_stage = [&](int kt) {
     const int later = min(R - 2, k_tiles - 2 - kt);  // stages after kt + 1 in flight
-    if (R >= 5 && later >= 3) wait_vm<(R >= 5 ? 3 : 0) * PW>();
+    // (with skipped loads a stage holds fewer than PW of this wave's loads: wait for all)
+    if (PART) wait_vm<0>();
+    else if (R >= 5 && later >= 3) wait_vm<(R >= 5 ? 3 : 0) * PW>();
     else if (R >= 4 && later >= 2) wait_vm<(R >= 4 ? 2 : 0) * PW>();
     else if (R >= 3 && later >= 1) wait_vm<PW>();
     else wait_vm<0>();
@@ -453,11 +464,11 @@ static hipError_t launch_tiled_one(const void *A, int64_t lda, int64_t M, int64_
                         ? tiled_split_tiles(static_cast<int64_t>(ntm) * ntn, sp.n_cu, sp.max_tiles)
                         : 0;
   const int n_whole = ntm * ntn - split;
-  hipExtLaunchKernelGGL((k_tiled<EPI, SP, NW, RING>), dim3(n_whole + 2 * split), dim3(NW * 64), 0, s,
-                        t.start, t.stop, 0, static_cast<const uint16_t *>(A), lda,
-                        static_cast<int>(M), k_total, static_cast<const u32x4_t *>(W),
-                        static_cast<int>(K / kFragK), ntm, ntn, out, ldo,
-                        static_cast<int>(n_store), static_cast<int>(ks_out), n_whole,
+  auto kern = grp.n_groups > 0 ? k_tiled<EPI, SP, NW, RING, true> : k_tiled<EPI, SP, NW, RING, false>;
+  hipExtLaunchKernelGGL(kern, dim3(n_whole + 2 * split), dim3(NW * 64), 0, s, t.start, t.stop, 0,
+                        static_cast<const uint16_t *>(A), lda, static_cast<int>(M), k_total,
+                        static_cast<const u32x4_t *>(W), static_cast<int>(K / kFragK), ntm, ntn,
+                        out, ldo, static_cast<int>(n_store), static_cast<int>(ks_out), n_whole,
                         static_cast<uint64_t *>(sp.buf), sp.cnt, grp);
   return hipGetLastError();
 }
