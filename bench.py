@@ -207,22 +207,55 @@ def run_decode_graph(lib, ranks, red_args, steps, warmup):
     return t1 - t0, g
 
 
+def _sleep_cycles_per_ms():
+    """Rate of torch's bounded spin kernel (cycles per ms), measured on the device."""
+    import torch
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    start.record()
+    torch.cuda._sleep(2_000_000)
+    stop.record()
+    torch.cuda.synchronize()
+    return 2_000_000 / max(start.elapsed_time(stop), 1e-3)
+
+
+EAGER_CHUNK = 16         # timed decode steps queued behind one spin kernel
+EAGER_HOST_MS = 0.6      # host time to enqueue one event-timed step (generous)
+
+
 def run_decode_eager(lib, ranks, red_args, steps, warmup):
-    """`steps` eager decode steps, every kernel timed by events attached to its launch."""
+    """`steps` eager decode steps, every kernel timed by events attached to its launch.
+
+    Returns the wall time of `steps` plain eager steps, and the per-launch durations of
+    the gate/up and down kernels.  Enqueuing a step from Python takes longer than the
+    GPU needs to run it, so launches issued one by one would each start on an idle
+    GPU, unlike the back-to-back kernels of the graph replays in the timed region.
+    The timed steps therefore go in chunks queued behind a bounded spin kernel
+    (long enough for the host to enqueue the whole chunk), each chunk led by one
+    untimed step, so that every timed launch runs right after the previous kernel."""
     import torch
     sp = _stream_ptr()
     for _ in range(warmup):
         decode_step(lib, ranks, red_args, sp)
-    pool = EventPool(4 * len(ranks) * steps)
-    hooks = [[pool.take4() for _ in ranks] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for st in range(steps):
-        decode_step(lib, ranks, red_args, sp, hooks[st])
+    for _ in range(steps):
+        decode_step(lib, ranks, red_args, sp)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for r in ranks:
-        lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
+    pool = EventPool(4 * len(ranks) * steps)
+    hooks = [[pool.take4() for _ in ranks] for _ in range(steps)]
+    rate = _sleep_cycles_per_ms()
+    torch.cuda.synchronize()
+    for c0 in range(0, steps, EAGER_CHUNK):
+        n = min(EAGER_CHUNK, steps - c0)
+        torch.cuda._sleep(int(rate * EAGER_HOST_MS * (n + 1)))
+        decode_step(lib, ranks, red_args, sp)
+        for st in range(c0, c0 + n):
+            decode_step(lib, ranks, red_args, sp, hooks[st])
+        for r in ranks:
+            lib.tp_mlp_shard_set_timing_events(r.args[0], None, 0)
+        torch.cuda.synchronize()
     k1 = [evs[0].elapsed_time(evs[1]) for per_step in hooks for _, evs in per_step]
     k2 = [evs[2].elapsed_time(evs[3]) for per_step in hooks for _, evs in per_step]
     return (t1 - t0), k1, k2
@@ -745,7 +778,7 @@ def main():
                 "median_launch_us": round(_median(k1) * 1e3, 2),
                 "min_launch_us": round(min(k1) * 1e3, 2), "launches": len(k1),
                 "timing": "HIP events attached to each launch (start/end of execution), "
-                          "eager pass of the same steps right after the timed replays"}
+                          "eager pass of the same steps right after the timed replays, queued %d at a time behind a bounded spin kernel so the timed launches run back to back as in the replays" % EAGER_CHUNK}
     down = {"kernel": "k_stream<OUT_F32> (down projection, decode shard M=32)",
             "algorithmic_bytes_per_launch": k2_bytes, "avg_launch_us": round(k2_ms * 1e3, 2),
             "median_launch_us": round(_median(k2) * 1e3, 2),
