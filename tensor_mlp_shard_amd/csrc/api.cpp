@@ -182,6 +182,8 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
   h->hidden = z.hidden_bytes ? base + o_hid : nullptr;
   h->scratch = z.scratch_floats ? reinterpret_cast<float *>(base + o_sk) : nullptr;
   h->counters = z.n_counters ? reinterpret_cast<int *>(base + o_cnt) : nullptr;
+  h->scratch_floats = z.scratch_floats;
+  h->n_counters = z.n_counters;
 
   const bool silu = d.act == TPM_ACT_SILU_GATE;
   const int64_t a_cols = silu ? 2 * d.ffn_shard : d.ffn_shard;
@@ -246,10 +248,14 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
 
   int path = d.path;
   if (path == TPM_PATH_AUTO) path = M <= kStreamMaxTokens ? TPM_PATH_STREAM : TPM_PATH_TILED;
+  StreamScratch ws;
+  ws.buf = h->scratch;
+  ws.cnt = h->counters;
+  ws.floats = h->scratch_floats;
+  ws.n_counters = h->n_counters;
   if (path == TPM_PATH_STREAM)
     e = launch_stream_gemm(epi1, stream_plan(M, h->n1 / kFragN, h->ks1), X_dev, d.d_model, M,
-                           h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, h->scratch,
-                           h->counters, s, t1);
+                           h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, ws, s, t1);
   TiledSplit split;
   if (h->scratch && h->counters && h->split_tiles > 0) {
     split.buf = h->scratch;
@@ -264,7 +270,7 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
     if (path == TPM_PATH_STREAM)
       e = launch_stream_gemm(epi2, stream_plan(M, h->n2 / kFragN, h->ks2), h->hidden, 0, M,
                              h->ks2, h->w2, h->n2 / kFragN, partial_dev, d.d_model, d.d_model, 0,
-                             h->scratch, h->counters, s, t2);
+                             ws, s, t2);
     else
       e = launch_tiled_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
                             d.d_model, d.d_model, 0, split, s, t2);

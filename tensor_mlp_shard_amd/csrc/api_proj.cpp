@@ -38,6 +38,7 @@ struct Proj {
   void *w;           // packed W (bf16) or a copy (fp32)
   float *scratch;    // contraction slices (streaming) / split halves (tiled)
   int *counters;     // arrival counters, zero between calls
+  int64_t scratch_floats, n_counters;  // room in scratch and counters
   int split_tiles;
   void *alloc_base;
 };
@@ -136,6 +137,8 @@ tpm_status tp_proj_create(const tpm_proj_desc *desc, const void *W_dev, void *st
   h->w = base;
   h->scratch = z.scratch_floats ? reinterpret_cast<float *>(base + o_sk) : nullptr;
   h->counters = z.n_counters ? reinterpret_cast<int *>(base + o_cnt) : nullptr;
+  h->scratch_floats = z.scratch_floats;
+  h->n_counters = z.n_counters;
   if (d.in_dtype == TPM_BF16) {
     e = launch_pack_bf16(W_dev, d.out_features, d.in_features, d.out_features, false,
                          d.out_features, z.n_pad / kFragN, h->ks, h->w, s);
@@ -177,8 +180,13 @@ tpm_status tp_proj_fwd(tpm_proj_t handle, const void *X_dev, int64_t M, void *Y_
   if (path == TPM_PATH_AUTO) path = M <= kStreamMaxTokens ? TPM_PATH_STREAM : TPM_PATH_TILED;
   hipError_t e;
   if (path == TPM_PATH_STREAM) {
+    StreamScratch ws;
+    ws.buf = h->scratch;
+    ws.cnt = h->counters;
+    ws.floats = h->scratch_floats;
+    ws.n_counters = h->n_counters;
     e = launch_stream_gemm(epi, stream_plan(M, h->n_pad / kFragN, h->ks), X_dev, K, M, h->ks, h->w,
-                           h->n_pad / kFragN, Y_dev, N, N, 0, h->scratch, h->counters, s);
+                           h->n_pad / kFragN, Y_dev, N, N, 0, ws, s);
   } else {
     TiledSplit split;
     if (h->scratch && h->counters && h->split_tiles > 0) {

@@ -329,13 +329,19 @@ hipError_t launch_stream_nw(const void *A, int64_t lda, int64_t M, int64_t ks, c
 template <int EPI, int MT, int C>
 hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
                              int64_t n_cb, int S, void *out, int64_t ldo, int64_t n_store,
-                             int64_t ks_out, float *scratch, int *counters, hipStream_t s,
+                             int64_t ks_out, const StreamScratch &ws, hipStream_t s,
                              const Timing &t = Timing()) {
   const int64_t groups = (M + 32 * MT - 1) / (32 * MT);
   const int64_t n_units = n_cb / C;
   const int64_t blocks = n_units * S * groups;
-  if (n_cb % C || S < 1 || (S > 1 && (!scratch || !counters)) || blocks > 0x7fffffff)
+  if (n_cb % C || S < 1 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // Slices park MT * C blocks of 1024 sums per workgroup and count in per (group, unit):
+  // refuse a launch whose scratch or counters would not fit the caller's workspace.
+  if (S > 1 && (!ws.buf || !ws.cnt || groups * n_units * S * MT * C * 1024 > ws.floats ||
+                groups * n_units > ws.n_counters))
     return hipErrorInvalidConfiguration;
+  float *scratch = ws.buf;
+  int *counters = ws.cnt;
   if (stream_waves(tokens_row_major(EPI), S) == 4)
     return launch_stream_nw<EPI, MT, C, 4>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
                                            ks_out, scratch, counters, s, t);
@@ -349,6 +355,10 @@ StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
   p.c = 1;
   p.s = 1;
   const int64_t groups = (M + 32 * p.mt - 1) / (32 * p.mt);
+  // Contraction slices only for a single token group (M <= 64, the decode sizes): the
+  // handles size their slice scratch and arrival counters for one group, and more
+  // token groups give more workgroups anyway.
+  if (groups > 1) return p;
   // One column block per workgroup over the whole contraction is the fastest shape
   // whenever there are enough blocks to occupy most compute units (measured at the
   // 70B-class decode shapes: wider groups or contraction slices only add traffic or
@@ -371,35 +381,35 @@ StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
 template <int E>
 static hipError_t launch_epi(const StreamPlan &plan, const void *A, int64_t lda, int64_t M,
                              int64_t ks, const void *W, int64_t n_cb, void *out, int64_t ldo,
-                             int64_t n_store, int64_t ks_out, float *scratch, int *counters,
+                             int64_t n_store, int64_t ks_out, const StreamScratch &ws,
                              hipStream_t s, const Timing &t) {
   if (plan.c != 1) return hipErrorInvalidConfiguration;  // wider groups are not instantiated
   if (plan.mt == 1)
     return launch_stream_cfg<E, 1, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
-                                      scratch, counters, s, t);
+                                      ws, s, t);
   return launch_stream_cfg<E, 2, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
-                                    scratch, counters, s, t);
+                                    ws, s, t);
 }
 
 hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, int64_t lda,
                               int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
-                              int64_t ldo, int64_t n_store, int64_t ks_out, float *scratch,
-                              int *counters, hipStream_t s, const Timing &t) {
+                              int64_t ldo, int64_t n_store, int64_t ks_out, const StreamScratch &ws,
+                              hipStream_t s, const Timing &t) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_epi<EPI_SILU_GATE>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_SILU_GATE>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_TANH:
-      return launch_epi<EPI_TANH>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_TANH>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_IDENTITY:
-      return launch_epi<EPI_IDENTITY>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_IDENTITY>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_OUT_F32:
-      return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_OUT_BF16:
-      return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_PROJ_F32:
-      return launch_epi<EPI_PROJ_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_PROJ_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     case EPI_PROJ_BF16:
-      return launch_epi<EPI_PROJ_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, scratch, counters, s, t);
+      return launch_epi<EPI_PROJ_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
     default:
       return hipErrorInvalidValue;
   }

@@ -99,6 +99,8 @@ struct Shard {
   void *hidden;       // packed H (bf16 path) or [max_tokens x F] fp32
   float *scratch;     // streaming path: per-slice partial sums
   int *counters;      // arrival counters (streaming slices, tiled halves), zero between calls
+  int64_t scratch_floats;  // room in scratch
+  int64_t n_counters;      // room in counters
   int n_cu;           // compute units of the device
   int split_tiles;    // tiled path: split tiles the scratch holds
   void *alloc_base;   // single device allocation holding everything above
@@ -119,8 +121,19 @@ struct StreamPlan {
 };
 
 // The streaming shape the library uses for M tokens against n_cb column blocks
-// and ks k-steps.
+// and ks k-steps.  Contraction slices (s > 1) only come with one token group
+// (M <= 64).
 StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks);
+
+// Workspace of the streaming contraction slices: sums parked by the slices
+// (`floats` of room) and the per-unit arrival counters (`n_counters` of room,
+// zero between calls).
+struct StreamScratch {
+  float *buf = nullptr;
+  int *cnt = nullptr;
+  int64_t floats = 0;
+  int64_t n_counters = 0;
+};
 
 // Optional timing of one launch: the events ride on the kernel's own dispatch
 // (start and end of its execution), so timing adds no work to the stream.
@@ -143,12 +156,14 @@ hipError_t launch_pack_bf16(const void *src, int64_t ld, int64_t K, int64_t ncol
 //   First product (epi = SILU_GATE / TANH / IDENTITY): A = X row-major [M x lda],
 //   out = packed H with ks_out k-steps.  Second product (epi = OUT_*): A = packed H
 //   with ks k-steps, out = row-major partial [M x ldo], columns < n_store stored.
-//   plan.s > 1 needs scratch (n_cb * plan.s * plan.mt * 1024 floats) and
-//   n_cb / plan.c zeroed counters.
+//   plan.s > 1 needs groups * n_cb * plan.s * plan.mt * 1024 floats of scratch and
+//   groups * n_cb / plan.c zeroed counters (groups = token groups of 32 plan.mt
+//   rows); a launch that would not fit `ws` is refused.
 hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, int64_t lda,
                               int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
-                              int64_t ldo, int64_t n_store, int64_t ks_out, float *scratch,
-                              int *counters, hipStream_t s, const Timing &t = Timing());
+                              int64_t ldo, int64_t n_store, int64_t ks_out,
+                              const StreamScratch &ws, hipStream_t s,
+                              const Timing &t = Timing());
 
 // Zero n ints (a plain kernel, so it may be captured in a graph).
 hipError_t launch_zero_i32(int *p, int64_t n, hipStream_t s);

@@ -150,6 +150,27 @@ def test_stream_sliced_contraction_narrow_shard(M):
     assert err <= TOL_BF16
 
 
+def test_stream_forced_many_token_groups_narrow_shard():
+    """The streaming path forced past one token group (M > 64) on a narrow shard
+    with a long contraction: the plan slices the contraction only for a single
+    token group, whose scratch and arrival counters the handle holds.  Sliced and
+    unsliced calls alternate on one handle (the counters must return to zero)."""
+    d, ffn = 8192, 1024  # per-rank F = 128 at tp=8: 8 gate/up column blocks
+    spec = synth.ModelSpec(d_model=d, ffn=ffn, pieces=8)
+    a, b = spec.shard(6, 8)
+    sh = tpm.Shard(a.to(DEV), b.to(DEV), "silu_gate", max_tokens=200, path="stream")
+    try:
+        for M in (32, 128, 200, 65, 32):
+            x = synth.tokens(M, d)
+            say("forced stream, narrow shard", "M", M, "d", d, "F", b.shape[0])
+            p = sh.forward(x.to(DEV)).cpu()
+            err = oracle.rel_err(p, oracle.shard_forward(x, a, b, "silu_gate"))
+            say("err", err)
+            assert err <= TOL_BF16
+    finally:
+        sh.close()
+
+
 def test_m_zero_is_noop():
     spec = synth.ModelSpec(d_model=256, ffn=512, pieces=8)
     a, b = spec.shard(0, 2)

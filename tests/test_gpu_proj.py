@@ -56,6 +56,22 @@ def test_o_shard_tp8(M):
     assert oracle.rel_err(y[rows], oracle.projection(a[rows], wo)) <= TOL_BF16
 
 
+def test_stream_forced_many_token_groups_narrow_projection():
+    """A narrow projection (8 column blocks) with a long contraction on the forced
+    streaming path: one token group slices the contraction, several do not."""
+    g = torch.Generator().manual_seed(77)
+    w = (torch.randn(8192, 256, generator=g) * 0.02).to(torch.bfloat16)
+    p = tpm.Projection(w.to(DEV), max_tokens=200, out_dtype=torch.float32, path="stream")
+    try:
+        for M in (32, 200, 96, 32):
+            x = synth.tokens(M)
+            say("forced stream, narrow projection M", M)
+            y = p.forward(x.to(DEV)).cpu()
+            assert oracle.rel_err(y, oracle.projection(x, w)) <= TOL_BF16
+    finally:
+        p.close()
+
+
 @pytest.mark.parametrize("K,N,M", [(64, 1, 3), (128, 100, 70), (192, 257, 1), (512, 700, 513)])
 def test_ragged_shapes_both_paths(K, N, M):
     g = torch.Generator().manual_seed(K + N + M)
