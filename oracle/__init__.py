@@ -23,6 +23,11 @@ It follows the pages' statement of the method:
 * page "大模型推理系统揭秘（07）Multi-GPU", section 1.2.4: the attention block's
   QKV projection is column-parallel and its output projection row-parallel
   (``projection``, one matrix product);
+* page "LLM 推理并行化：先找瓶颈，再决定怎么切", section 三.4 (decode context
+  parallelism): each rank attends over its own part of the KV history and reports
+  its local score maximum, its sum of exponentials and its exponential-weighted sum
+  of values; the merge rescales every rank to the global maximum and divides the
+  summed values by the summed exponentials (``attn_partials_merge``);
 * page "7.4 推理侧并行", section 7.4.2 (communication quantization): partials travel as FP8 with a
   per-token scale and are summed in high precision (``e4m3_value``,
   ``e4m3_encode``, ``quantize_fp8``, ``reduce_fp8``).  FP8 is the OCP E4M3 format,
@@ -217,6 +222,45 @@ def reduce_add_rmsnorm(partials, residual, gamma, eps: float):
     ms = np.mean(h * h, axis=1, keepdims=True)
     y = h / np.sqrt(ms + float(eps)) * g[None, :]
     return h, y
+
+
+def attn_partials_merge(values, maxima, expsums):
+    """Merge of k attention partials, in fp64 (page "LLM 推理并行化", section 三.4).
+
+    ``values[i]`` [rows, dim], ``maxima[i]`` and ``expsums[i]`` [rows]: rank i's
+    exponential-weighted value sum, local score maximum and sum of exponentials,
+    both taken relative to that maximum.  In the page's order: the global maximum
+    over the ranks, each rank's scale ``exp(m_i - max)``, the denominator
+    ``sum_i scale_i * s_i`` and numerator ``sum_i scale_i * v_i`` (rank order), and
+    their quotient.  Returns ``(out [rows, dim], max [rows], expsum [rows])``: the
+    merged output and the merged statistics (the denominator is the merged sum of
+    exponentials relative to the global maximum), so a merged result can be
+    merged again.  A row with no keys on any rank (every maximum -inf) is taken as
+    an empty attention: output 0, maximum -inf, sum 0.
+    """
+    if not (len(values) == len(maxima) == len(expsums)) or not values:
+        raise ValueError("need matching, non-empty lists of partials")
+    v = [_f64(x) for x in values]
+    m = [_f64(x) for x in maxima]
+    e = [_f64(x) for x in expsums]
+    rows, dim = v[0].shape
+    for vi, mi, ei in zip(v, m, e):
+        if vi.shape != (rows, dim) or mi.shape != (rows,) or ei.shape != (rows,):
+            raise ValueError("partials must be [rows, dim] with [rows] statistics")
+    gmax = m[0].copy()
+    for mi in m[1:]:
+        gmax = np.maximum(gmax, mi)
+    empty = np.isneginf(gmax)
+    ref = np.where(empty, 0.0, gmax)  # any finite reference for empty rows
+    scales = [np.where(np.isneginf(mi), 0.0, np.exp(mi - ref)) for mi in m]
+    den = np.zeros(rows)
+    num = np.zeros((rows, dim))
+    for sc, ei, vi in zip(scales, e, v):
+        den = den + sc * ei
+        num = num + sc[:, None] * vi
+    safe = np.where(empty | (den == 0.0), 1.0, den)
+    out = np.where(empty[:, None], 0.0, num / safe[:, None])
+    return out, gmax, np.where(empty, 0.0, den)
 
 
 def e4m3_value(code: int) -> float:
