@@ -30,6 +30,8 @@ The JSON line also carries
   that follow it, against the same work in two launches;
 * ``fp8_partials``: the decode partials quantized to FP8 with per-row scales and
   summed in fp32, against the fp32 sum (time, wire bytes, transport error);
+* ``attn_partials_merge``: the decode-context-parallel merge of 8 ranks' attention
+  partials (32 tokens x 64 heads, head width 128) on one GPU;
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
   same decode workload.
 
@@ -670,6 +672,41 @@ def run_fp8_partials(lib, dev, reps=200):
     return out
 
 
+ATTN_HEADS, HEAD_DIM = 64, 128
+
+
+def run_attn_merge(tpm, synth, dev, reps=200):
+    """Merge of the attention partials of 8 decode-context-parallel ranks for one
+    decode step (32 tokens x 64 query heads = 2048 rows, head width 128, fp32 values
+    and statistics, fp32 output plus merged statistics), many calls per HIP graph."""
+    import torch
+    rows, dim, k = M_DECODE * ATTN_HEADS, HEAD_DIM, TP
+    vals, maxs, sums = synth.attn_partials(rows, dim, k)
+    vals = [v.to(dev) for v in vals]
+    maxs = [m.to(dev) for m in maxs]
+    sums = [e.to(dev) for e in sums]
+    out = torch.empty(rows, dim, device=dev)
+    mo = torch.empty(rows, device=dev)
+    eo = torch.empty(rows, device=dev)
+
+    def merge(sp):  # the binding launches on torch's current stream (the capture stream)
+        tpm.tp_attn_partials_merge(vals, maxs, sums, out, mo, eo)
+    inner = 50
+    g = _graph_of(_repeat(merge, inner))
+    t = _time_graph(g, max(4, reps // inner)) / inner
+    del g
+    torch.cuda.synchronize()
+    nbytes = k * rows * dim * 4 + 2 * k * rows * 4 + rows * dim * 4 + 2 * rows * 4
+    gbs = nbytes / t / 1e9
+    log("attention partials merge: %.2f us, %.1f GB/s" % (t * 1e6, gbs))
+    return {"rows": rows, "dim": dim, "k": k, "us_per_call": round(t * 1e6, 2),
+            "algorithmic_bytes": nbytes, "GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "note": "8 ranks' partials (weighted value sums [2048 x 128] fp32, per-row maxima "
+                    "and sums of exponentials) merged to the attention output and merged "
+                    "statistics; many calls per HIP graph, time per call"}
+
+
 def cpu_baseline(host_inputs, budget_s=12.0):
     """The fp64 oracle on the host over whole decode steps (8 shards at M = 32 plus
     the partials sum) until about `budget_s` seconds of oracle compute have run."""
@@ -832,7 +869,7 @@ def main():
         log("tensor-parallel degree sweep ...")
         sweep, all_shards = run_sweep(tpm, lib, dev, host_inputs[1:])
 
-    reduce_norm = fp8 = attn = moe = None
+    reduce_norm = fp8 = attn = moe = attn_merge = None
     if not args.no_sweep:
         log("attention projections ...")
         attn = run_attention_projections(tpm, lib, synth, dev)
@@ -842,6 +879,8 @@ def main():
         reduce_norm = run_reduce_norm(lib, dev)
         log("fp8 partials ...")
         fp8 = run_fp8_partials(lib, dev)
+        log("attention partials merge ...")
+        attn_merge = run_attn_merge(tpm, synth, dev)
 
     if args.calib_copy:
         calib_copy(dev)
@@ -877,6 +916,7 @@ def main():
         "grouped_experts": moe,
         "reduce_add_rmsnorm": reduce_norm,
         "fp8_partials": fp8,
+        "attn_partials_merge": attn_merge,
         "cpu_baseline": cpu,
         "device": props.name,
         "device_peaks": device_peaks(props),

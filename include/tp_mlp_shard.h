@@ -230,6 +230,39 @@ tpm_status tp_partials_reduce_fp8(const void *const *q_dev, const float *const *
                                   int32_t k, int64_t rows, int64_t cols, void *out_dev,
                                   int32_t out_dtype, void *stream);
 
+/* Merge of k attention partials held on one GPU.
+ *
+ * Page "LLM 推理并行化：先找瓶颈，再决定怎么切", section 三.4 (decode context
+ * parallelism): the stored KV history is split by sequence position; each rank
+ * attends over its own keys and reports, per query row, its local score maximum
+ * m_i, its sum of exponentials s_i = sum_j exp(z_j - m_i) and its weighted value
+ * sum v_i = sum_j exp(z_j - m_i) V_j.  The merge rescales every rank to the global
+ * maximum (so no exponential exceeds 1):
+ *   g[r]      = max_i m_i[r]
+ *   c_i       = exp(m_i[r] - g[r])                 (0 for a rank with m_i = -inf)
+ *   S[r]      = sum_i c_i * s_i[r]                 (rank order, fp32)
+ *   out[r][:] = (sum_i c_i * v_i[r][:]) / S[r]     (rank order, fp32)
+ * A row with no keys on any rank (every m_i = -inf) gives out = 0, g = -inf, S = 0.
+ *
+ *   values_dev   host array of k device pointers, each [rows x dim] of in_dtype
+ *                (TPM_F32 or TPM_BF16), 16-byte aligned.
+ *   max_dev      host array of k device pointers, each [rows] fp32 (m_i).
+ *   expsum_dev   host array of k device pointers, each [rows] fp32 (s_i).
+ *   k            1 <= k <= 16.
+ *   rows         >= 0 (0 is a no-op); dim: a multiple of 8, 8 <= dim <= 2^20.
+ *   out_dev      [rows x dim] of out_dtype, 16-byte aligned; may be values_dev[0]
+ *                exactly when in_dtype == out_dtype, must not overlap the others.
+ *   max_out_dev, expsum_out_dev
+ *                [rows] fp32 each, the merged statistics (g, S), so that the merged
+ *                result (out * S, g, S) can be merged again; both NULL to skip.
+ *                They must not overlap any input.
+ * Statistics pointers need 4-byte alignment.  Bitwise reproducible from call to
+ * call.  Asynchronous on `stream`; allocates nothing. */
+tpm_status tp_attn_partials_merge(const void *const *values_dev, const float *const *max_dev,
+                                  const float *const *expsum_dev, int32_t k, int64_t rows,
+                                  int64_t dim, int32_t in_dtype, void *out_dev, int32_t out_dtype,
+                                  float *max_out_dev, float *expsum_out_dev, void *stream);
+
 /* Free a handle and its device memory (waits for the device first).  NULL is OK. */
 tpm_status tp_mlp_shard_destroy(tpm_shard_t h);
 

@@ -29,7 +29,7 @@ import os
 __all__ = [
     "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
     "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tp_partials_quantize_fp8",
-    "tp_partials_reduce_fp8", "tp_proj_create", "tp_proj_fwd", "tp_proj_destroy",
+    "tp_partials_reduce_fp8", "tp_attn_partials_merge", "attn_partials_merge", "tp_proj_create", "tp_proj_fwd", "tp_proj_destroy",
     "Projection", "tp_moe_create", "tp_moe_fwd", "tp_moe_destroy", "GroupedExperts",
     "tpm_status_str", "tp_mlp_shard_set_timing_events", "Shard",
     "partials_reduce", "tensor_parallel_output", "TpmError", "LIB_PATH", "ACT", "PATH",
@@ -110,6 +110,10 @@ def capi():
     lib.tp_partials_reduce_fp8.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i64, i64,
                                            vp, i32, vp]
     lib.tp_partials_reduce_fp8.restype = ctypes.c_int
+    lib.tp_attn_partials_merge.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                           ctypes.POINTER(vp), i32, i64, i64, i32, vp, i32, vp,
+                                           vp, vp]
+    lib.tp_attn_partials_merge.restype = ctypes.c_int
     lib.tp_proj_create.argtypes = [ctypes.POINTER(TpmProjDesc), vp, vp, ctypes.POINTER(vp)]
     lib.tp_proj_create.restype = ctypes.c_int
     lib.tp_proj_fwd.argtypes = [vp, vp, i64, vp, vp]
@@ -282,6 +286,55 @@ def tp_partials_reduce_fp8(qs, scales, out, stream=None) -> None:
            "tp_partials_reduce_fp8")
 
 
+def tp_attn_partials_merge(values, maxima, expsums, out, max_out=None, expsum_out=None,
+                           stream=None) -> None:
+    """Merge k attention partials (page "LLM 推理并行化", section 三.4): values[i]
+    [rows, dim] (float32 or bfloat16), maxima[i] and expsums[i] float32 [rows];
+    out [rows, dim]; optional merged statistics max_out, expsum_out float32 [rows]."""
+    torch = _torch()
+    vals, maxs, sums = list(values), list(maxima), list(expsums)
+    if not vals or not (len(vals) == len(maxs) == len(sums)):
+        raise ValueError("need matching, non-empty lists of values, maxima and expsums")
+    if vals[0].dim() != 2:
+        raise ValueError("values must be [rows, dim]")
+    rows, dim = vals[0].shape
+    in_dt = vals[0].dtype
+    for v, m, e in zip(vals, maxs, sums):
+        if tuple(v.shape) != (rows, dim) or v.dtype != in_dt:
+            raise ValueError("values must be [rows, dim] of one dtype")
+        if tuple(m.shape) != (rows,) or tuple(e.shape) != (rows,) or \
+                m.dtype != torch.float32 or e.dtype != torch.float32:
+            raise ValueError("maxima and expsums must be float32 [rows]")
+    if tuple(out.shape) != (rows, dim):
+        raise ValueError("out must be [rows, dim]")
+    if (max_out is None) != (expsum_out is None):
+        raise ValueError("give both merged statistics or neither")
+    if max_out is not None:
+        for t in (max_out, expsum_out):
+            if tuple(t.shape) != (rows,) or t.dtype != torch.float32:
+                raise ValueError("merged statistics must be float32 [rows]")
+    k = len(vals)
+    va = (ctypes.c_void_p * k)(*[_dev_ptr(v, "values") for v in vals])
+    ma = (ctypes.c_void_p * k)(*[_dev_ptr(m, "maxima") for m in maxs])
+    ea = (ctypes.c_void_p * k)(*[_dev_ptr(e, "expsums") for e in sums])
+    mo = _dev_ptr(max_out, "max_out") if max_out is not None else None
+    eo = _dev_ptr(expsum_out, "expsum_out") if expsum_out is not None else None
+    _check(capi().tp_attn_partials_merge(va, ma, ea, k, rows, dim, _dtype_code(in_dt),
+                                         _dev_ptr(out, "out"), _dtype_code(out.dtype), mo, eo,
+                                         _stream_ptr(stream)), "tp_attn_partials_merge")
+
+
+def attn_partials_merge(values, maxima, expsums, out_dtype=None, stream=None):
+    """Merged output and merged statistics (out, max, expsum) of k attention partials."""
+    torch = _torch()
+    v0 = values[0]
+    out = torch.empty(v0.shape, dtype=out_dtype or torch.float32, device=v0.device)
+    mo = torch.empty(v0.shape[0], dtype=torch.float32, device=v0.device)
+    eo = torch.empty_like(mo)
+    tp_attn_partials_merge(values, maxima, expsums, out, mo, eo, stream)
+    return out, mo, eo
+
+
 def tp_mlp_shard_destroy(handle: int) -> None:
     _check(capi().tp_mlp_shard_destroy(ctypes.c_void_p(handle)), "tp_mlp_shard_destroy")
 
@@ -452,11 +505,15 @@ class GroupedExperts:
     def forward(self, x, counts, out=None, stream=None):
         """x: [T, d] tokens grouped by expert; counts: int32 [E] on the GPU."""
         torch = _torch()
+        if x.dim() != 2 or x.shape[1] != self.d_model or x.dtype != torch.bfloat16:
+            raise ValueError("x must be [T, %d] of torch.bfloat16" % self.d_model)
         T = x.shape[0]
         if counts.dtype != torch.int32 or counts.numel() != self.n_experts:
             raise ValueError("counts must be int32 [%d]" % self.n_experts)
         if out is None:
             out = torch.empty((T, self.d_model), dtype=self.out_dtype, device=x.device)
+        elif tuple(out.shape) != (T, self.d_model) or out.dtype != self.out_dtype:
+            raise ValueError("out must be [%d, %d] of %s" % (T, self.d_model, self.out_dtype))
         tp_moe_fwd(self.handle, x, counts, T, out, stream)
         return out
 

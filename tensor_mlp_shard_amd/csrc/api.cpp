@@ -351,6 +351,36 @@ tpm_status tp_partials_reduce_fp8(const void *const *q_dev, const float *const *
                                     static_cast<hipStream_t>(stream)));
 }
 
+tpm_status tp_attn_partials_merge(const void *const *values_dev, const float *const *max_dev,
+                                  const float *const *expsum_dev, int32_t k, int64_t rows,
+                                  int64_t dim, int32_t in_dtype, void *out_dev, int32_t out_dtype,
+                                  float *max_out_dev, float *expsum_out_dev, void *stream) {
+  if (!values_dev || !max_dev || !expsum_dev || !out_dev) return TPM_ERR_INVALID_ARG;
+  if (in_dtype != TPM_F32 && in_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (out_dtype != TPM_F32 && out_dtype != TPM_BF16) return TPM_ERR_INVALID_ARG;
+  if (!max_out_dev != !expsum_out_dev) return TPM_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxParts || rows < 0 || dim < 8 || dim % 8 || dim > (int64_t(1) << 20) ||
+      rows > (int64_t(1) << 40) / dim)
+    return TPM_ERR_SHAPE;
+  auto stat_aligned = [](const void *p) { return reinterpret_cast<uintptr_t>(p) % 4 == 0; };
+  for (int i = 0; i < k; ++i) {
+    if (!values_dev[i] || !max_dev[i] || !expsum_dev[i]) return TPM_ERR_INVALID_ARG;
+    if (!aligned(values_dev[i]) || !stat_aligned(max_dev[i]) || !stat_aligned(expsum_dev[i]))
+      return TPM_ERR_ALIGN;
+    if (max_out_dev && (max_out_dev == max_dev[i] || expsum_out_dev == expsum_dev[i] ||
+                        max_out_dev == expsum_dev[i] || expsum_out_dev == max_dev[i]))
+      return TPM_ERR_INVALID_ARG;
+  }
+  if (!aligned(out_dev)) return TPM_ERR_ALIGN;
+  if (max_out_dev && (!stat_aligned(max_out_dev) || !stat_aligned(expsum_out_dev)))
+    return TPM_ERR_ALIGN;
+  if (out_dev == values_dev[0] && in_dtype != out_dtype) return TPM_ERR_INVALID_ARG;
+  if (rows == 0) return TPM_OK;
+  return from_hip(launch_attn_merge(values_dev, max_dev, expsum_dev, k, rows, dim, in_dtype,
+                                    out_dev, out_dtype, max_out_dev, expsum_out_dev,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 tpm_status tp_mlp_shard_destroy(tpm_shard_t handle) {
   Shard *h = reinterpret_cast<Shard *>(handle);
   if (!h) return TPM_OK;

@@ -240,4 +240,125 @@ hipError_t launch_reduce_norm(const void *const *parts, int k, int64_t rows, int
              : launch_norm2<TPM_BF16, TPM_BF16>(pp, k, rows, cols8, res_in, res_out, gamma, eps, y, out_dtype, s);
 }
 
+// ---------------------------------------------------------------------------
+// Merge of k attention partials held on one GPU (page "LLM 推理并行化：先找瓶颈，再决定
+// 怎么切", section 三.4, decode context parallelism: each rank attends over its own
+// part of the KV history and reports its local score maximum m_i, its sum of
+// exponentials s_i and its exponential-weighted value sum v_i, all relative to
+// m_i).  Per row: g = max_i m_i, c_i = exp(m_i - g), out = (sum_i c_i v_i) /
+// (sum_i c_i s_i), sums in rank order in fp32.  A rank without keys (m_i = -inf)
+// has c_i = 0; a row without keys on any rank gives 0.  Optionally the merged
+// statistics (g, sum_i c_i s_i) are written, so that a merged result can be merged
+// again.
+//
+// One thread per 8 values of a row: it reads the row's 2k statistics (cache hits
+// for all but the first thread of the row), then the k value chunks, 8 ranks' loads
+// in flight at a time.  HBM-bound.
+struct StatPtrs {
+  const float *p[kMaxParts];
+};
+
+template <int IN, int OUT>
+__global__ void __launch_bounds__(256)
+k_attn_merge(PartPtrs vp, StatPtrs mp, StatPtrs sp, int k, int64_t rows, int dim8,
+             void *__restrict__ out, float *__restrict__ m_out, float *__restrict__ s_out) {
+  const int64_t gstride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t n = rows * dim8;
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < n;
+       c += gstride) {
+    const int64_t r = c / dim8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float den = 0.0f, g = -INFINITY;
+    // Rescaled sums of ranks [i0, i0 + 8) in rank order (the statistics and value
+    // chunks already in registers).
+    auto add8 = [&](int i0, const float (&mi)[8], const float (&si)[8], const float (&v)[8][8]) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (i0 + q >= k) break;
+        const float ci = mi[q] == -INFINITY ? 0.0f : expf(mi[q] - g);
+        den += ci * si[q];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += ci * v[q][j];
+      }
+    };
+    // The loads of up to 8 ranks are issued together (k is uniform, so the guards
+    // are scalar branches).
+    auto load_ranks = [&](int i0, float (&mi)[8], float (&si)[8], float (&v)[8][8]) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        mi[q] = -INFINITY;
+        if (i0 + q < k) {
+          mi[q] = mp.p[i0 + q][r];
+          si[q] = sp.p[i0 + q][r];
+          load8<IN>(vp.p[i0 + q], c, v[q]);
+        }
+      }
+    };
+    float mi[8], si[8], v[8][8];
+    if (k <= 8) {
+      // One round of loads: maxima, sums and values together.
+      load_ranks(0, mi, si, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) g = fmaxf(g, mi[q]);
+      if (g != -INFINITY) add8(0, mi, si, v);
+    } else {
+      // The global maximum first, then the ranks 8 at a time.
+      for (int i0 = 0; i0 < k; i0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t[q] = i0 + q < k ? mp.p[i0 + q][r] : -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g = fmaxf(g, t[q]);
+      }
+      if (g != -INFINITY) {
+        for (int i0 = 0; i0 < k; i0 += 8) {
+          load_ranks(i0, mi, si, v);
+          add8(i0, mi, si, v);
+        }
+      }
+    }
+    if (g != -INFINITY) {
+      const float d = den != 0.0f ? den : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = acc[j] / d;
+    }
+    store8<OUT>(out, c, acc);
+    if (m_out && c - r * dim8 == 0) {
+      m_out[r] = g;
+      s_out[r] = den;
+    }
+  }
+}
+
+hipError_t launch_attn_merge(const void *const *values, const float *const *maxima,
+                             const float *const *expsums, int k, int64_t rows, int64_t dim,
+                             int in_dtype, void *out, int out_dtype, float *max_out,
+                             float *expsum_out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (k < 1 || k > kMaxParts || dim % 8 || dim < 8 || dim / 8 > 0x7fffffff)
+    return hipErrorInvalidValue;
+  PartPtrs vp = {};
+  StatPtrs mp = {}, sp = {};
+  for (int i = 0; i < k; ++i) {
+    vp.p[i] = values[i];
+    mp.p[i] = maxima[i];
+    sp.p[i] = expsums[i];
+  }
+  const int dim8 = static_cast<int>(dim / 8);
+  const int64_t n = rows * dim8;
+  constexpr int kThreads = 64;
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 8192) blocks = 8192;
+  dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (in_dtype == TPM_F32 && out_dtype == TPM_F32)
+    hipLaunchKernelGGL((k_attn_merge<TPM_F32, TPM_F32>), grid, block, 0, s, vp, mp, sp, k, rows, dim8, out, max_out, expsum_out);
+  else if (in_dtype == TPM_F32)
+    hipLaunchKernelGGL((k_attn_merge<TPM_F32, TPM_BF16>), grid, block, 0, s, vp, mp, sp, k, rows, dim8, out, max_out, expsum_out);
+  else if (out_dtype == TPM_F32)
+    hipLaunchKernelGGL((k_attn_merge<TPM_BF16, TPM_F32>), grid, block, 0, s, vp, mp, sp, k, rows, dim8, out, max_out, expsum_out);
+  else
+    hipLaunchKernelGGL((k_attn_merge<TPM_BF16, TPM_BF16>), grid, block, 0, s, vp, mp, sp, k, rows, dim8, out, max_out, expsum_out);
+  return hipGetLastError();
+}
+
 }  // namespace tpm

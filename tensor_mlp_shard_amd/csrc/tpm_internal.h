@@ -218,6 +218,14 @@ hipError_t launch_reduce_norm(const void *const *parts, int k, int64_t rows, int
                               const void *gamma, float eps, void *y, int out_dtype,
                               hipStream_t s);
 
+// Merge of k attention partials (values [rows x dim], per-row maxima and sums of
+// exponentials, fp32 statistics); dim a multiple of 8.  max_out / expsum_out may be
+// null (both or neither).
+hipError_t launch_attn_merge(const void *const *values, const float *const *maxima,
+                             const float *const *expsums, int k, int64_t rows, int64_t dim,
+                             int in_dtype, void *out, int out_dtype, float *max_out,
+                             float *expsum_out, hipStream_t s);
+
 // FP8 (E4M3) partials with one scale per row: quantize one partial, and the
 // rank-order fp32 sum of k quantized partials.  cols a multiple of 16; the
 // quantizer holds a row in registers (1024 threads x 2 chunks of 16).

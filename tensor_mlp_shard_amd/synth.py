@@ -250,3 +250,24 @@ def sample_rows(M: int, n: int, seed: int = 7) -> list[int]:
     perm = torch.randperm(M - 2, generator=g)[: max(n - 2, 0)] + 1
     rows = sorted(set([0, M - 1] + perm.tolist()))
     return rows
+
+
+def attn_partials(rows: int, dim: int, k: int, keys_per_rank: int = 1024, seed: int = 8100,
+                  dtype=torch.float32):
+    """Synthetic attention partials of k ranks for `rows` query rows (tokens x heads)
+    with value width `dim`, shaped like a split KV history of `keys_per_rank` keys per
+    rank: per rank and row a local maximum m ~ N(3, 1), a sum of exponentials
+    s ~ U(1, keys_per_rank) (the key at the maximum contributes exactly 1), and a
+    weighted value sum v = sqrt(s) * N(0, 1) in `dtype`.  Returns lists
+    (values [rows, dim], maxima [rows], expsums [rows]); statistics are float32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    vals, maxs, sums = [], [], []
+    for _ in range(k):
+        m = torch.randn(rows, generator=g, dtype=torch.float32) + 3.0
+        e = 1.0 + torch.rand(rows, generator=g, dtype=torch.float32) * (keys_per_rank - 1)
+        v = torch.randn(rows, dim, generator=g, dtype=torch.float32) * e.sqrt()[:, None]
+        vals.append(v.to(dtype))
+        maxs.append(m)
+        sums.append(e)
+    return vals, maxs, sums

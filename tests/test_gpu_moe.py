@@ -108,3 +108,25 @@ def test_full_size_expert_layer_sampled():
     say("16 experts d 8192, F 2048, tokens", sum(counts))
     x, w1, w2, (y,) = run(spec, counts)
     check(x, counts, w1, w2, y, rows=synth.sample_rows(sum(counts), 48))
+
+
+def test_binding_refuses_mismatched_tokens_and_output():
+    spec = synth.ExpertSpec(d_model=256, ffn_expert=128, n_experts=2)
+    w1, w2 = spec.weights()
+    g = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), max_tokens=64)
+    try:
+        counts = torch.tensor([8, 8], dtype=torch.int32, device=DEV)
+        good = torch.zeros(16, 256, dtype=torch.bfloat16, device=DEV)
+        with pytest.raises(ValueError):
+            g.forward(torch.zeros(16, 128, dtype=torch.bfloat16, device=DEV), counts)
+        with pytest.raises(ValueError):
+            g.forward(good.float(), counts)
+        with pytest.raises(ValueError):
+            g.forward(good, counts, out=torch.empty(8, 256, device=DEV))
+        with pytest.raises(ValueError):
+            g.forward(good, counts, out=torch.empty(16, 256, dtype=torch.bfloat16, device=DEV))
+        y = g.forward(good, counts)
+        torch.cuda.synchronize()
+        assert y.shape == (16, 256) and torch.all(y == 0)
+    finally:
+        g.close()
