@@ -768,7 +768,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no cross-GPU path (no collectives); "
+        print("bench.py measures one GPU: the library has no cross-GPU path (no collectives); "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
