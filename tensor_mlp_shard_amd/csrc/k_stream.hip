@@ -30,6 +30,8 @@
 
 namespace tpm {
 
+static_assert(kStreamMaxSlices <= 16, "the hand-off holds every slice's sums in registers");
+
 // Launch shapes.  C column blocks per workgroup: every token fragment a wave loads
 // feeds C products, so the token operand costs 1/C of the weight traffic through
 // the vector caches.  D k-steps per load batch (two batches in flight per wave),
@@ -286,13 +288,28 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       __syncthreads();
-      for (int e = tid; e < 1024; e += NT) {
-        float *p = scratch + (wg_slot * BLK + m * C + c) * 1024 + e;
-        // coherent loads: read at the device coherence point, never from a stale line
-        float a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int q = 1; q < S; ++q)
-          a += __hip_atomic_load(p + static_cast<int64_t>(q) * BLK * 1024, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+      // Every slice's sums of this thread's elements are loaded before any is added,
+      // so the hand-off costs one round trip to the coherence point, not one per
+      // slice.  Coherent loads: read at the device coherence point, never from a
+      // stale line.
+      constexpr int EPT = 1024 / NT;
+      float t[EPT][kStreamMaxSlices];
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        float *p = scratch + (wg_slot * BLK + m * C + c) * 1024 + tid + j * NT;
+#pragma unroll
+        for (int q = 0; q < kStreamMaxSlices; ++q)
+          if (q < S)
+            t[j][q] = __hip_atomic_load(p + static_cast<int64_t>(q) * BLK * 1024, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        float a = t[j][0];
+#pragma unroll
+        for (int q = 1; q < kStreamMaxSlices; ++q)  // slice order
+          if (q < S) a += t[j][q];
+        const int e = tid + j * NT;
         vsum[e >> 6][e & 63] = a;
       }
       __syncthreads();
