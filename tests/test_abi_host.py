@@ -247,3 +247,32 @@ def test_moe_validation(lib):
         assert not h.value
     assert lib.tp_moe_fwd(None, None, None, 0, None, None) == INVALID
     assert lib.tp_moe_destroy(None) == OK
+
+
+def test_attn_merge_validation(lib):
+    v, m, e = _ptrs(0x1000, 0x2000), _ptrs(0x5000, 0x6000), _ptrs(0x7000, 0x8000)
+    out = ctypes.c_void_p(0x3000)
+    mo, eo = ctypes.c_void_p(0x9000), ctypes.c_void_p(0xa000)
+    f = lib.tp_attn_partials_merge
+    assert f(None, m, e, 2, 4, 16, 0, out, 0, None, None, None) == INVALID
+    assert f(v, None, e, 2, 4, 16, 0, out, 0, None, None, None) == INVALID
+    assert f(v, m, e, 2, 4, 16, 0, None, 0, None, None, None) == INVALID
+    assert f(v, m, e, 2, 4, 16, 3, out, 0, None, None, None) == INVALID   # dtype
+    assert f(v, m, e, 2, 4, 16, 0, out, 0, mo, None, None) == INVALID     # one statistic only
+    assert f(v, m, e, 0, 4, 16, 0, out, 0, None, None, None) == SHAPE
+    assert f(_ptrs(*([0x1000] * 17)), _ptrs(*([0x5000] * 17)), _ptrs(*([0x7000] * 17)),
+             17, 4, 16, 0, out, 0, None, None, None) == SHAPE
+    assert f(v, m, e, 2, -1, 16, 0, out, 0, None, None, None) == SHAPE
+    assert f(v, m, e, 2, 4, 12, 0, out, 0, None, None, None) == SHAPE   # dim not a multiple of 8
+    assert f(v, m, e, 2, 4, 0, 0, out, 0, None, None, None) == SHAPE
+    assert f(_ptrs(0x1000, None), m, e, 2, 4, 16, 0, out, 0, None, None, None) == INVALID
+    assert f(_ptrs(0x1000, 0x2008), m, e, 2, 4, 16, 0, out, 0, None, None, None) == ALIGN
+    assert f(v, _ptrs(0x5000, 0x6002), e, 2, 4, 16, 0, out, 0, None, None, None) == ALIGN
+    assert f(v, m, e, 2, 4, 16, 0, ctypes.c_void_p(0x3004), 0, None, None, None) == ALIGN
+    # merged statistics may not land on an input's statistics
+    assert f(v, m, e, 2, 4, 16, 0, out, 0, ctypes.c_void_p(0x6000), eo, None) == INVALID
+    assert f(v, m, e, 2, 4, 16, 0, out, 0, mo, ctypes.c_void_p(0x7000), None) == INVALID
+    # in place over rank 0's values needs the same dtype
+    assert f(v, m, e, 2, 4, 16, 0, ctypes.c_void_p(0x1000), 1, None, None, None) == INVALID
+    # rows = 0 is a no-op that never touches the device
+    assert f(v, m, e, 2, 0, 16, 0, out, 0, mo, eo, None) == OK
