@@ -69,7 +69,7 @@ class TpmMoeDesc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int64), ("ffn_expert", ctypes.c_int64),
                 ("n_experts", ctypes.c_int64), ("max_tokens", ctypes.c_int64),
                 ("act", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 class TpmError(RuntimeError):
@@ -488,7 +488,7 @@ class GroupedExperts:
     gate then up columns) or [E, d, F]; w2: [E, F, d]; bf16 on the GPU."""
 
     def __init__(self, w1, w2, activation="silu_gate", max_tokens=8192, out_dtype=None,
-                 stream=None):
+                 path="auto", stream=None):
         torch = _torch()
         if w1.dim() != 3 or w2.dim() != 3 or w1.shape[0] != w2.shape[0]:
             raise ValueError("w1 [E, d, n1] and w2 [E, F, d] with the same E")
@@ -499,7 +499,7 @@ class GroupedExperts:
         self.out_dtype = out_dtype if out_dtype is not None else torch.float32
         self.max_tokens = int(max_tokens)
         self.desc = TpmMoeDesc(d, F, E, self.max_tokens, ACT[activation], _dtype_code(w1.dtype),
-                               _dtype_code(self.out_dtype), 0)
+                               _dtype_code(self.out_dtype), PATH[path])
         self.handle = tp_moe_create(self.desc, w1, w2, stream)
 
     def forward(self, x, counts, out=None, stream=None):

@@ -49,6 +49,7 @@ tpm_status check_moe_desc(const tpm_moe_desc *d) {
   if (d->ffn_expert < 1 || d->ffn_expert > (int64_t(1) << 20)) return TPM_ERR_SHAPE;
   if (d->n_experts < 1 || d->n_experts > kMaxExperts) return TPM_ERR_SHAPE;
   if (d->max_tokens < 0 || d->max_tokens > (int64_t(1) << 24)) return TPM_ERR_SHAPE;
+  if (d->path < TPM_PATH_AUTO || d->path > TPM_PATH_TILED) return TPM_ERR_INVALID_ARG;
   return TPM_OK;
 }
 
@@ -145,8 +146,16 @@ tpm_status tp_moe_fwd(tpm_moe_t handle, const void *X_dev, const int32_t *counts
   g1.w_stride = h->w1_stride;
   g2.w_stride = h->w2_stride;
   const TiledSplit none;
-  hipError_t e = launch_tiled_gemm(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->n1, h->hidden, 0,
-                                   0, h->ks2, none, s, Timing(), g1);
+  // First projection: weight streaming at a hundred or so tokens per expert, the
+  // tiled matrix-core kernel for more (both write the same hidden layout).
+  const bool stream_first =
+      d.path == TPM_PATH_STREAM || (d.path == TPM_PATH_AUTO && T <= kGroupStreamRows * d.n_experts);
+  hipError_t e = stream_first
+                     ? launch_group_stream(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->w1_stride,
+                                           h->n1 / kFragN, counts_dev, g1.n_groups, h->hidden,
+                                           h->ks2, s)
+                     : launch_tiled_gemm(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->n1,
+                                         h->hidden, 0, 0, h->ks2, none, s, Timing(), g1);
   if (e == hipSuccess)
     e = launch_tiled_gemm(epi2, h->hidden, 0, T, h->ffn_pad, h->w2, h->n2, Y_dev, d.d_model,
                           d.d_model, 0, none, s, Timing(), g2);

@@ -1,0 +1,209 @@
+// First projection of the grouped expert MLP at small token counts per expert.
+//
+// Page "大模型推理系统揭秘（07）Multi-GPU", MoE section: the tokens routed to the
+// experts of one GPU are laid out contiguously by expert and all experts' products
+// run as one batched job.  At decode-like loads (a hundred or so tokens per
+// expert) every weight element meets few tokens, so the product is bound by
+// streaming the experts' weights from HBM, as in the dense decode kernel
+// (k_stream.hip), not by the matrix cores.
+//
+//  * A workgroup owns 8 column blocks (256 columns) of one expert's packed first
+//    weight for one tile of up to 128 of that expert's tokens; each of its 8 waves
+//    owns one 32-column block over the whole contraction and streams it straight
+//    into registers (1 KiB non-temporal loads, the next stage in flight).  No two
+//    waves read the same weight fragment, so the weights never pass through LDS.
+//  * The tile's tokens are the operand all 8 waves share: per stage of 64
+//    contraction indices each wave loads 16 token rows as 128-byte row segments and
+//    writes them to a double-buffered LDS tile (row stride padded against bank
+//    conflicts), one barrier per stage, and every wave reads its MFMA fragments
+//    from there.  Token bytes per weight byte: 128 / 256.
+//  * Tiles are mapped to experts through the token counts in device memory: tile
+//    row t counts through the experts' 128-row tiles in expert order; a workgroup
+//    past the last tile exits.  Hidden rows of an expert start on a 256-row
+//    boundary, the layout the tiled second projection reads.
+//  * The epilogue applies SiLU(gate) * up (lane c meets lane c + 16 of the same
+//    block), tanh or identity per wave and writes the packed hidden buffer.  Token
+//    rows of a partly filled 32-row block past the expert's tokens repeat its last
+//    token (finite values, never part of an output row); blocks wholly past them
+//    are neither computed nor written.
+#include "device_common.h"
+#include "tpm_internal.h"
+
+namespace tpm {
+
+namespace {
+
+constexpr int kGsRows = static_cast<int>(kGroupStreamRows);  // token rows per tile
+constexpr int kGsWaves = 8;     // waves per workgroup = column blocks per tile
+constexpr int kGsXStride = 72;  // staged token row stride in bf16 (64 + 8 padding)
+
+template <int EPI>
+__global__ void __launch_bounds__(kGsWaves * 64)
+k_group_stream(const uint16_t *__restrict__ X, int64_t lda, int T, int ks,
+               const u32x4_t *__restrict__ W, int64_t w_stride, int n_cb,
+               const int *__restrict__ counts, int n_groups, u32x4_t *__restrict__ hidden,
+               int ks_out) {
+  static_assert(writes_hidden(EPI), "first projection only");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGsRows][kGsXStride];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[kGsWaves][32][40];  // h of one block per wave
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // Expert and row tile of this workgroup (uniform over the workgroup).
+  int rt = blockIdx.y, off = 0, hoff = 0, g = 0, n = 0;
+  for (; g < n_groups; ++g) {
+    n = min(max(counts[g], 0), T - off);
+    const int tiles = (n + kGsRows - 1) / kGsRows;
+    if (rt < tiles) break;
+    rt -= tiles;
+    off += n;
+    hoff += (n + kTileM - 1) / kTileM * kTileM;
+  }
+  if (g == n_groups) return;
+  const int row0 = off + rt * kGsRows;                 // first token row of the tile
+  const int rows = min(kGsRows, off + n - row0);       // tokens in the tile (>= 1)
+  const int hrow0 = hoff + rt * kGsRows;               // first hidden row of the tile
+  const int nvb = (rows + 31) >> 5;                    // 32-row blocks holding tokens
+  const int cb = blockIdx.x * kGsWaves + wave;         // this wave's column block
+
+  const u32x4_t *wp = W + static_cast<int64_t>(g) * w_stride + static_cast<int64_t>(cb) * 64 + lane;
+  // The 16 token rows this wave stages per stage: two loads of 8 rows x 128 bytes.
+  const uint16_t *xr[2];
+  int srow[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * wave + 8 * q + (lane >> 3);
+    srow[q] = r;
+    xr[q] = X + static_cast<int64_t>(row0 + min(r, rows - 1)) * lda + 8 * (lane & 7);
+  }
+  const int nst = ks / 4;  // stages of 4 k-steps
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
+
+  // Loads of stage st (clamped to the last stage: valid addresses, never used).
+  u32x4_t w0[4], w1[4], x0[2], x1[2];
+  auto load = [&](u32x4_t (&wb)[4], u32x4_t (&xb)[2], int st) {
+    const int s = min(st, nst - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // streamed once: non-temporal
+      wb[i] = __builtin_nontemporal_load(&wp[static_cast<int64_t>(4 * s + i) * n_cb * 64]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) xb[q] = *reinterpret_cast<const u32x4_t *>(xr[q] + 64 * s);
+  };
+  auto stage_tokens = [&](const u32x4_t (&xb)[2], int buf) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<u32x4_t *>(&xs[buf][srow[q]][8 * (lane & 7)]) = xb[q];
+  };
+  // Products of stage st: 4 k-steps x the row blocks holding tokens.  The fragment
+  // of k-step ksi for row 32 m + l % 32 holds contraction indices
+  // 32 (ksi / 2) + 16 (l / 32) + 8 (ksi % 2) .. + 7 of the stage (fragment order).
+  auto compute = [&](const u32x4_t (&wb)[4], int buf, int st) {
+    const bool valid = st < nst;
+#pragma unroll
+    for (int ksi = 0; ksi < 4; ++ksi) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < nvb) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t *>(
+              &xs[buf][32 * m + (lane & 31)][32 * (ksi >> 1) + 16 * (lane >> 5) + 8 * (ksi & 1)]);
+          const u32x4_t zero = {0u, 0u, 0u, 0u};
+          acc[m] = mfma_32x32x16(valid ? a : zero, wb[ksi], acc[m]);
+        }
+      }
+    }
+  };
+
+  // Stage st's tokens sit in LDS buffer st % 2 (written before the barrier that
+  // precedes its products), its weights in registers; stage st + 1 is in flight.
+  // A buffer is rewritten only after the barrier that follows its last reads.
+  load(w0, x0, 0);
+  stage_tokens(x0, 0);
+  load(w1, x1, 1);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    compute(w0, 0, st);
+    stage_tokens(x1, 1);
+    load(w0, x0, st + 2);
+    __syncthreads();
+    compute(w1, 1, st + 1);
+    stage_tokens(x0, 0);
+    load(w1, x1, st + 3);
+    __syncthreads();
+  }
+
+  // Epilogue per wave and row block: the activation into LDS as bf16, then the
+  // packed hidden chunks (8 features of one row per 16 bytes).
+  constexpr int JW = (EPI == EPI_SILU_GATE) ? 16 : 32;  // features of this column block
+  const int j0 = cb * JW;
+  uint16_t (*h)[40] = hs[wave];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= nvb) break;
+    const int c = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int R = mfma32_row(r, lane);
+      const float v = acc[m][r];
+      if constexpr (EPI == EPI_SILU_GATE) {
+        const float up = __shfl_xor(v, 16);
+        if (c < 16) h[R][c] = f32_to_bf16(silu_f(v) * up);
+      } else {
+        h[R][c] = f32_to_bf16(act_f<EPI>(v));
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int e = lane; e < 32 * (JW / 8); e += 64) {
+      const int R = e & 31, q = e >> 5;
+      const int j = j0 + 8 * q;
+      const int s = 2 * (j >> 5) + ((j >> 3) & 1);
+      const int ln = 32 * ((j >> 4) & 1) + R;
+      const int hrow = hrow0 + 32 * m;  // the 32-row block of hidden rows
+      hidden[(static_cast<int64_t>(hrow >> 5) * ks_out + s) * 64 + ln] =
+          *reinterpret_cast<const u32x4_t *>(&h[R][8 * q]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+}
+
+}  // namespace
+
+hipError_t launch_group_stream(int epi, const void *X, int64_t lda, int64_t T, int64_t K,
+                               const void *W, int64_t w_stride, int64_t n_cb, const int *counts,
+                               int n_groups, void *hidden, int64_t ks_out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (K % 64 || n_cb % kGsWaves || n_groups < 1) return hipErrorInvalidValue;
+  const int64_t tiles_y = (T + kGsRows - 1) / kGsRows + n_groups;  // >= the sum of the experts' tiles
+  if (tiles_y > 65535 || n_cb / kGsWaves > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(n_cb / kGsWaves), static_cast<unsigned>(tiles_y));
+  dim3 block(kGsWaves * 64);
+  const uint16_t *x = static_cast<const uint16_t *>(X);
+  const u32x4_t *w = static_cast<const u32x4_t *>(W);
+  u32x4_t *hb = static_cast<u32x4_t *>(hidden);
+  const int t = static_cast<int>(T), ks = static_cast<int>(K / kFragK), nc = static_cast<int>(n_cb);
+  const int ko = static_cast<int>(ks_out);
+  switch (epi) {
+    case EPI_SILU_GATE:
+      hipLaunchKernelGGL(k_group_stream<EPI_SILU_GATE>, grid, block, 0, s, x, lda, t, ks, w, w_stride, nc, counts, n_groups, hb, ko);
+      break;
+    case EPI_TANH:
+      hipLaunchKernelGGL(k_group_stream<EPI_TANH>, grid, block, 0, s, x, lda, t, ks, w, w_stride, nc, counts, n_groups, hb, ko);
+      break;
+    case EPI_IDENTITY:
+      hipLaunchKernelGGL(k_group_stream<EPI_IDENTITY>, grid, block, 0, s, x, lda, t, ks, w, w_stride, nc, counts, n_groups, hb, ko);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tpm

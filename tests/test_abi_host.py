@@ -231,17 +231,18 @@ def test_proj_validation(lib):
 
 def test_moe_validation(lib):
     def create(**kw):
-        base = dict(d=512, F=256, E=4, T=64, act=1, ind=tpm.BF16, outd=tpm.F32)
+        base = dict(d=512, F=256, E=4, T=64, act=1, ind=tpm.BF16, outd=tpm.F32, path=0)
         base.update(kw)
         d = tpm.TpmMoeDesc(base["d"], base["F"], base["E"], base["T"], base["act"], base["ind"],
-                           base["outd"], 0)
+                           base["outd"], base["path"])
         h = ctypes.c_void_p()
         rc = lib.tp_moe_create(ctypes.byref(d), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
                                None, ctypes.byref(h))
         return rc, h
     for kw, code in [({"act": 5}, INVALID), ({"ind": tpm.F32}, INVALID), ({"outd": 4}, INVALID),
                      ({"d": 100}, SHAPE), ({"d": 0}, SHAPE), ({"F": 0}, SHAPE), ({"E": 0}, SHAPE),
-                     ({"E": 1025}, SHAPE), ({"T": -1}, SHAPE)]:
+                     ({"E": 1025}, SHAPE), ({"T": -1}, SHAPE), ({"path": 3}, INVALID),
+                     ({"path": -1}, INVALID)]:
         rc, h = create(**kw)
         assert rc == code, kw
         assert not h.value

@@ -22,11 +22,12 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run(spec, counts, T=None, act="silu_gate", out_dtype=torch.float32, seed=5, reps=1):
+def run(spec, counts, T=None, act="silu_gate", out_dtype=torch.float32, seed=5, reps=1, path="auto"):
     w1, w2 = spec.weights(act)
     T = sum(counts) if T is None else T
     x = synth.tokens(T, d=spec.d_model, seed=seed)
-    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), act, max_tokens=max(T, 1), out_dtype=out_dtype)
+    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), act, max_tokens=max(T, 1), out_dtype=out_dtype,
+                            path=path)
     try:
         c = torch.tensor(counts, dtype=torch.int32, device=DEV)
         outs = []
@@ -66,47 +67,57 @@ def check(x, counts, w1, w2, y, act="silu_gate", rows=None):
     assert err <= TOL_BF16
 
 
-def test_page_example_counts():
+PATHS = ["stream", "tiled"]  # first projection: weight streaming or matrix-core tiles
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_page_example_counts(path):
     spec = synth.ExpertSpec(d_model=1024, ffn_expert=512, n_experts=3)
     counts = [128, 64, 96]
-    x, w1, w2, (y,) = run(spec, counts)
+    x, w1, w2, (y,) = run(spec, counts, path=path)
     check(x, counts, w1, w2, y)
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("act", ["silu_gate", "tanh", "identity"])
-def test_ragged_and_empty_groups(act):
+def test_ragged_and_empty_groups(act, path):
+    """Experts of 0, 1 and 255-300 tokens: several 128-row tiles per expert on the
+    streaming path, partly filled 256-row tiles on the tiled one."""
     spec = synth.ExpertSpec(d_model=512, ffn_expert=300, n_experts=6)
     counts = [0, 300, 1, 255, 256, 257]
-    x, w1, w2, (y,) = run(spec, counts, act=act)
+    x, w1, w2, (y,) = run(spec, counts, act=act, path=path)
     check(x, counts, w1, w2, y, act)
 
 
-def test_sixteen_experts_bf16_out_and_deterministic():
+@pytest.mark.parametrize("path", PATHS)
+def test_sixteen_experts_bf16_out_and_deterministic(path):
     spec = synth.ExpertSpec(d_model=2048, ffn_expert=1024, n_experts=16)
     counts = synth.expert_counts(16)
-    x, w1, w2, ys = run(spec, counts, out_dtype=torch.bfloat16, reps=2)
+    x, w1, w2, ys = run(spec, counts, out_dtype=torch.bfloat16, reps=2, path=path)
     assert torch.equal(ys[0], ys[1])
     check(x, counts, w1, w2, ys[0], rows=synth.sample_rows(sum(counts), 200))
 
 
-def test_counts_past_the_rows_are_clamped_and_rows_past_the_counts_untouched():
+@pytest.mark.parametrize("path", PATHS)
+def test_counts_past_the_rows_are_clamped_and_rows_past_the_counts_untouched(path):
     spec = synth.ExpertSpec(d_model=256, ffn_expert=128, n_experts=4)
     # the counts claim 40 + 50 + 60 + 70 rows, X holds 100: experts 0, 1 and the first
     # 10 rows of expert 2 are computed, nothing past row 100 is read or written
-    x, w1, w2, (y,) = run(spec, [40, 50, 60, 70], T=100)
+    x, w1, w2, (y,) = run(spec, [40, 50, 60, 70], T=100, path=path)
     check(x, [40, 50, 60, 70], w1, w2, y)
     # counts summing to less than T: rows past the sum keep their old value
-    x, w1, w2, (y,) = run(spec, [10, -3, 5, 0], T=40)
+    x, w1, w2, (y,) = run(spec, [10, -3, 5, 0], T=40, path=path)
     check(x, [10, 0, 5, 0], w1, w2, y)
     assert torch.all(y[15:] == 7.0)
 
 
-def test_full_size_expert_layer_sampled():
+@pytest.mark.parametrize("path", PATHS)
+def test_full_size_expert_layer_sampled(path):
     """The 16 experts of one GPU at the 70B-class width (d 8192, expert width 2048)."""
     spec = synth.ExpertSpec()
     counts = synth.expert_counts(spec.n_experts)
-    say("16 experts d 8192, F 2048, tokens", sum(counts))
-    x, w1, w2, (y,) = run(spec, counts)
+    say("16 experts d 8192, F 2048, tokens", sum(counts), "first projection", path)
+    x, w1, w2, (y,) = run(spec, counts, path=path)
     check(x, counts, w1, w2, y, rows=synth.sample_rows(sum(counts), 48))
 
 
