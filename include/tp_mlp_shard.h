@@ -320,11 +320,10 @@ tpm_status tp_proj_destroy(tpm_proj_t h);
  * one grouped GEMM).  Routing, dispatch and combine (all-to-all exchanges, router
  * weights) are the caller's.
  *
- * The first projection runs on one of two kernels (the second always on the tiled
- * one): STREAM, for a hundred or so tokens per expert, streams each expert's first
- * weight once per 128 of its tokens (weight-bound, as at decode); TILED runs
- * 256-token tiles on the matrix cores (for many tokens per expert).  AUTO takes
- * STREAM when T <= 128 * E.
+ * Both projections run on one of two kernels: STREAM, for a hundred or so tokens
+ * per expert, streams each expert's weights once per 128 of its tokens
+ * (weight-bound, as at decode); TILED runs 256-token tiles on the matrix cores (for
+ * many tokens per expert).  AUTO takes STREAM when T <= 128 * E.
  *
  *   d_model     d, a multiple of 64.
  *   ffn_expert  F: hidden features of one expert (no multiple constraint).
@@ -341,7 +340,7 @@ typedef struct tpm_moe_desc {
   int32_t act;
   int32_t in_dtype;
   int32_t out_dtype;
-  int32_t path;  /* tpm_path: AUTO, STREAM or TILED (first projection) */
+  int32_t path;  /* tpm_path: AUTO, STREAM or TILED */
 } tpm_moe_desc;
 
 typedef struct tpm_moe *tpm_moe_t;

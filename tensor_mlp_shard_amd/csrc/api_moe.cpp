@@ -146,19 +146,22 @@ tpm_status tp_moe_fwd(tpm_moe_t handle, const void *X_dev, const int32_t *counts
   g1.w_stride = h->w1_stride;
   g2.w_stride = h->w2_stride;
   const TiledSplit none;
-  // First projection: weight streaming at a hundred or so tokens per expert, the
-  // tiled matrix-core kernel for more (both write the same hidden layout).
-  const bool stream_first =
+  // Weight streaming at a hundred or so tokens per expert, the tiled matrix-core
+  // kernel for more (both read and write the same hidden layout).
+  const bool streamed =
       d.path == TPM_PATH_STREAM || (d.path == TPM_PATH_AUTO && T <= kGroupStreamRows * d.n_experts);
-  hipError_t e = stream_first
+  hipError_t e = streamed
                      ? launch_group_stream(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->w1_stride,
-                                           h->n1 / kFragN, counts_dev, g1.n_groups, h->hidden,
+                                           h->n1 / kFragN, counts_dev, g1.n_groups, h->hidden, 0, 0,
                                            h->ks2, s)
                      : launch_tiled_gemm(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->n1,
                                          h->hidden, 0, 0, h->ks2, none, s, Timing(), g1);
   if (e == hipSuccess)
-    e = launch_tiled_gemm(epi2, h->hidden, 0, T, h->ffn_pad, h->w2, h->n2, Y_dev, d.d_model,
-                          d.d_model, 0, none, s, Timing(), g2);
+    e = streamed ? launch_group_stream(epi2, h->hidden, 0, T, h->ffn_pad, h->w2, h->w2_stride,
+                                       h->n2 / kFragN, counts_dev, g2.n_groups, Y_dev, d.d_model,
+                                       d.d_model, 0, s)
+                 : launch_tiled_gemm(epi2, h->hidden, 0, T, h->ffn_pad, h->w2, h->n2, Y_dev,
+                                     d.d_model, d.d_model, 0, none, s, Timing(), g2);
   return from_hip(e);
 }
 

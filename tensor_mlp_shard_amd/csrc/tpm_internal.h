@@ -203,15 +203,18 @@ hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int
                              int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
                              const Timing &t = Timing(), const TiledGroups &grp = TiledGroups());
 
-// First projection of the grouped expert MLP by weight streaming: tiles of up to
+// Either projection of the grouped expert MLP by weight streaming: tiles of up to
 // kGroupStreamRows of one expert's tokens by 256 columns, each wave streaming one
-// 32-column block of the expert's packed first weight; same operands, counts and
-// hidden layout as the grouped tiled product (epi: SILU_GATE, TANH or IDENTITY).
-// n_cb a multiple of 8, K of 64.
+// 32-column block of the expert's packed weight; same operands, counts and hidden
+// layout as the grouped tiled product.  epi SILU_GATE, TANH or IDENTITY: A is X
+// (row stride lda) and out the packed hidden buffer with ks_out k-steps.  epi
+// OUT_F32 or OUT_BF16: A is the packed hidden buffer (K / 16 k-steps) and out the
+// row-major output (row stride ldo, columns < n_store).  n_cb a multiple of 8, K of 64.
 constexpr int64_t kGroupStreamRows = 128;
-hipError_t launch_group_stream(int epi, const void *X, int64_t lda, int64_t T, int64_t K,
+hipError_t launch_group_stream(int epi, const void *A, int64_t lda, int64_t T, int64_t K,
                                const void *W, int64_t w_stride, int64_t n_cb, const int *counts,
-                               int n_groups, void *hidden, int64_t ks_out, hipStream_t s);
+                               int n_groups, void *out, int64_t ldo, int64_t n_store,
+                               int64_t ks_out, hipStream_t s);
 
 hipError_t launch_f32_gemm(int epi, const float *A, int64_t lda, int64_t M, int64_t K,
                            const float *B, int64_t ldb, int64_t N, int64_t up_offset, void *out,

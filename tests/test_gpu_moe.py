@@ -67,7 +67,7 @@ def check(x, counts, w1, w2, y, act="silu_gate", rows=None):
     assert err <= TOL_BF16
 
 
-PATHS = ["stream", "tiled"]  # first projection: weight streaming or matrix-core tiles
+PATHS = ["stream", "tiled"]  # both projections: weight streaming or matrix-core tiles
 
 
 @pytest.mark.parametrize("path", PATHS)
@@ -82,7 +82,8 @@ def test_page_example_counts(path):
 @pytest.mark.parametrize("act", ["silu_gate", "tanh", "identity"])
 def test_ragged_and_empty_groups(act, path):
     """Experts of 0, 1 and 255-300 tokens: several 128-row tiles per expert on the
-    streaming path, partly filled 256-row tiles on the tiled one."""
+    streaming path (partly filled 32-row blocks, empty blocks skipped in both
+    projections), partly filled 256-row tiles on the tiled one."""
     spec = synth.ExpertSpec(d_model=512, ffn_expert=300, n_experts=6)
     counts = [0, 300, 1, 255, 256, 257]
     x, w1, w2, (y,) = run(spec, counts, act=act, path=path)
@@ -116,7 +117,7 @@ def test_full_size_expert_layer_sampled(path):
     """The 16 experts of one GPU at the 70B-class width (d 8192, expert width 2048)."""
     spec = synth.ExpertSpec()
     counts = synth.expert_counts(spec.n_experts)
-    say("16 experts d 8192, F 2048, tokens", sum(counts), "first projection", path)
+    say("16 experts d 8192, F 2048, tokens", sum(counts), "path", path)
     x, w1, w2, (y,) = run(spec, counts, path=path)
     check(x, counts, w1, w2, y, rows=synth.sample_rows(sum(counts), 48))
 
