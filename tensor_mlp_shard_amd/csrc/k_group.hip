@@ -11,10 +11,10 @@
 //  * A workgroup owns 8 column blocks (256 columns) of one expert's packed first
 //    weight for one tile of up to 128 of that expert's tokens; each of its 8 waves
 //    owns one 32-column block over the whole contraction and streams it straight
-//    into registers (1 KiB non-temporal loads, the next stage in flight).  No two
+//    into registers (1 KiB non-temporal loads, the next two stages in flight).  No two
 //    waves read the same weight fragment, so the weights never pass through LDS.
 //  * The tile's tokens are the operand all 8 waves share, staged per stage of 64
-//    contraction indices in a double-buffered LDS tile, one barrier per stage, and
+//    contraction indices in a 3-buffer LDS ring, one barrier per stage, and
 //    every wave reads its MFMA fragments from there.  First projection: each wave
 //    loads 16 token rows of X as 128-byte row segments (row stride padded against
 //    bank conflicts in LDS).  Second projection: the packed hidden buffer is already
@@ -24,14 +24,14 @@
 //  * Tiles are mapped to experts through the token counts in device memory: tile
 //    row t counts through the experts' 128-row tiles in expert order; a workgroup
 //    past the last tile exits.  Hidden rows of an expert start on a 256-row
-//    boundary, the layout the tiled second projection reads.
+//    boundary, the layout the tiled kernel uses.
 //  * First projection: the epilogue applies SiLU(gate) * up (lane c meets lane
 //    c + 16 of the same block), tanh or identity per wave and writes the packed
 //    hidden buffer.  Token rows of a partly filled 32-row block past the expert's
 //    tokens repeat its last token (finite values, never part of an output row);
-//    blocks wholly past them are neither computed nor written.  Second projection:
+//    blocks wholly past them are neither loaded nor written.  Second projection:
 //    the rows of the expert's tokens are stored row-major (fp32 or bf16); hidden
-//    blocks wholly past them are neither loaded nor computed.
+//    blocks wholly past them are not loaded.
 #include "device_common.h"
 #include "tpm_internal.h"
 
@@ -42,6 +42,7 @@ namespace {
 constexpr int kGsRows = static_cast<int>(kGroupStreamRows);  // token rows per tile
 constexpr int kGsWaves = 8;     // waves per workgroup = column blocks per tile
 constexpr int kGsXStride = 72;  // staged token row stride in bf16 (64 + 8 padding)
+constexpr int kGsDepth = 3;     // stages held at once: one being multiplied, the rest in flight
 
 // A: X row-major [T x lda] (first projection) or the packed hidden buffer with ks
 // k-steps (second); out: the packed hidden buffer with ks_out k-steps (first) or
@@ -54,7 +55,8 @@ k_group_stream(const uint16_t *__restrict__ A, int64_t lda, int T, int ks,
                int64_t ldo, int n_store, int ks_out) {
   constexpr bool FIRST = writes_hidden(EPI);
   // token stages: row segments (first projection) or fragments (second)
-  constexpr int XBYTES = FIRST ? 2 * kGsRows * kGsXStride * 2 : 2 * 16 * 1024;
+  constexpr int D = kGsDepth;
+  constexpr int XBYTES = FIRST ? D * kGsRows * kGsXStride * 2 : D * 16 * 1024;
   __shared__ __attribute__((aligned(16))) char smem[XBYTES];
   uint16_t (*xs)[kGsRows][kGsXStride] = reinterpret_cast<uint16_t (*)[kGsRows][kGsXStride]>(smem);
   u32x4_t (*fs)[16][64] = reinterpret_cast<u32x4_t (*)[16][64]>(smem);
@@ -99,7 +101,8 @@ k_group_stream(const uint16_t *__restrict__ A, int64_t lda, int T, int ks,
           ((static_cast<int64_t>(hrow0 >> 5) + (f >> 2)) * ks + (f & 3)) * 64 + lane);
     }
   }
-  const bool stage_own = FIRST || (2 * wave) / 4 < nvb;  // this wave's fragments hold tokens
+  // Both stage rows of 32-row block wave / 2: skipped for blocks holding no tokens.
+  const bool stage_own = (wave >> 1) < nvb;
   const int nst = ks / 4;  // stages of 4 k-steps
 
   f32x16_t acc[4];
@@ -109,70 +112,75 @@ k_group_stream(const uint16_t *__restrict__ A, int64_t lda, int T, int ks,
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
 
   // Loads of stage st (clamped to the last stage: valid addresses, never used).
-  u32x4_t w0[4], w1[4], x0[2], x1[2];
+  u32x4_t wb[D][4], xb[D][2];
   auto load = [&](u32x4_t (&wb)[4], u32x4_t (&xb)[2], int st) {
     const int s = min(st, nst - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // streamed once: non-temporal
       wb[i] = __builtin_nontemporal_load(&wp[static_cast<int64_t>(4 * s + i) * n_cb * 64]);
+    if (!stage_own) return;
     if constexpr (FIRST) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) xb[q] = *reinterpret_cast<const u32x4_t *>(xr[q] + 64 * s);
-    } else if (stage_own) {
+    } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q)  // 4 k-steps of 64 chunks per stage
         xb[q] = reinterpret_cast<const u32x4_t *>(xr[q])[static_cast<int64_t>(4 * s) * 64];
     }
   };
   auto stage_tokens = [&](const u32x4_t (&xb)[2], int buf) {
+    if (!stage_own) return;
     if constexpr (FIRST) {
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         *reinterpret_cast<u32x4_t *>(&xs[buf][srow[q]][8 * (lane & 7)]) = xb[q];
-    } else if (stage_own) {
+    } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q) fs[buf][srow[q]][lane] = xb[q];
     }
   };
-  // Products of stage st: 4 k-steps x the row blocks holding tokens.  The fragment
-  // of k-step ksi for row 32 m + l % 32 holds contraction indices
-  // 32 (ksi / 2) + 16 (l / 32) + 8 (ksi % 2) .. + 7 of the stage (fragment order).
+  // Products of stage st: 4 k-steps x 4 row blocks.  The fragment of k-step ksi for
+  // row 32 m + l % 32 holds contraction indices 32 (ksi / 2) + 16 (l / 32) +
+  // 8 (ksi % 2) .. + 7 of the stage (fragment order).  Row blocks holding no tokens
+  // are multiplied too, from whatever their LDS rows hold, so that no branch
+  // separates a fragment read from its product; a row of a product depends only on
+  // the same row of the token operand, and those rows are never stored.
   auto compute = [&](const u32x4_t (&wb)[4], int buf, int st) {
     const bool valid = st < nst;
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ksi = 0; ksi < 4; ++ksi) {
+      u32x4_t a[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        if (m < nvb) {
-          u32x4_t a;
-          if constexpr (FIRST)
-            a = *reinterpret_cast<const u32x4_t *>(
-                &xs[buf][32 * m + (lane & 31)][32 * (ksi >> 1) + 16 * (lane >> 5) + 8 * (ksi & 1)]);
-          else
-            a = fs[buf][4 * m + ksi][lane];
-          const u32x4_t zero = {0u, 0u, 0u, 0u};
-          acc[m] = mfma_32x32x16(valid ? a : zero, wb[ksi], acc[m]);
-        }
+        if constexpr (FIRST)
+          a[m] = *reinterpret_cast<const u32x4_t *>(
+              &xs[buf][32 * m + (lane & 31)][32 * (ksi >> 1) + 16 * (lane >> 5) + 8 * (ksi & 1)]);
+        else
+          a[m] = fs[buf][4 * m + ksi][lane];
       }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[m] = mfma_32x32x16(valid ? a[m] : zero, wb[ksi], acc[m]);
     }
   };
 
-  // Stage st's tokens sit in LDS buffer st % 2 (written before the barrier that
-  // precedes its products), its weights in registers; stage st + 1 is in flight.
-  // A buffer is rewritten only after the barrier that follows its last reads.
-  load(w0, x0, 0);
-  stage_tokens(x0, 0);
-  load(w1, x1, 1);
+  // Stage st's tokens sit in LDS buffer st % D (written before the barrier that
+  // precedes its products) and its weights in register set st % D; stages st + 1
+  // .. st + D - 1 are in flight.  A buffer is rewritten only after the barrier that
+  // follows its last reads (D - 1 barriers later).
+  load(wb[0], xb[0], 0);
+  stage_tokens(xb[0], 0);
+#pragma unroll
+  for (int j = 1; j < D; ++j) load(wb[j], xb[j], j);
   __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    compute(w0, 0, st);
-    stage_tokens(x1, 1);
-    load(w0, x0, st + 2);
-    __syncthreads();
-    compute(w1, 1, st + 1);
-    stage_tokens(x0, 0);
-    load(w1, x1, st + 3);
-    __syncthreads();
+  for (int st = 0; st < nst; st += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      compute(wb[j], j, st + j);
+      stage_tokens(xb[(j + 1) % D], (j + 1) % D);
+      load(wb[j], xb[j], st + j + D);
+      __syncthreads();
+    }
   }
 
   if constexpr (!FIRST) {
