@@ -45,6 +45,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -62,14 +63,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources and build flags, to tell whether stored counter
-    readings still describe the kernels that are built."""
+    """Hash of the kernel sources (comments and layout left out: they change no
+    kernel) and build flags, to tell whether stored counter readings still describe
+    the kernels that are built."""
     from tensor_mlp_shard_amd import build as b
     h = hashlib.sha256()
     for src in sorted(b.SOURCES) + ["device_common.h", "tpm_internal.h"]:
-        with open(os.path.join(b.CSRC, src), "rb") as f:
-            h.update(src.encode() + b"\0" + f.read())
+        with open(os.path.join(b.CSRC, src), encoding="utf-8") as f:
+            code = " ".join(_COMMENT.sub(" ", f.read()).split())
+        h.update(src.encode() + b"\0" + code.encode())
     h.update(" ".join(b.HIP_FLAGS[:-1]).encode())
     return h.hexdigest()[:16]
 
