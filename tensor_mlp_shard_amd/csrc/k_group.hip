@@ -8,11 +8,12 @@
 // streaming the experts' weights from HBM, as in the dense decode kernel
 // (k_stream.hip), not by the matrix cores.
 //
-//  * A workgroup owns 8 column blocks (256 columns) of one expert's packed first
-//    weight for one tile of up to 128 of that expert's tokens; each of its 8 waves
-//    owns one 32-column block over the whole contraction and streams it straight
-//    into registers (1 KiB non-temporal loads, the next two stages in flight).  No two
-//    waves read the same weight fragment, so the weights never pass through LDS.
+//  * A workgroup owns 8 column blocks (256 columns) of one expert's packed weight
+//    (either projection) for one tile of up to 128 of that expert's tokens; each
+//    of its 8 waves owns one 32-column block over the whole contraction and
+//    streams it straight into registers (1 KiB non-temporal loads, the next two
+//    stages in flight).  No two waves read the same weight fragment, so the
+//    weights never pass through LDS.
 //  * The tile's tokens are the operand all 8 waves share, staged per stage of 64
 //    contraction indices in a 3-buffer LDS ring, one barrier per stage, and
 //    every wave reads its MFMA fragments from there.  First projection: each wave
