@@ -359,7 +359,9 @@ tpm_status tp_moe_create(const tpm_moe_desc *desc, const void *W1_dev, const voi
  *               are clamped (rows of X beyond T are never read), negative counts
  *               count as 0, and rows beyond the sum of the counts are left as they
  *               were.
- *   T           rows of X and Y, 0 <= T <= max_tokens (0 is a no-op).
+ *   T           rows of X and Y, 0 <= T <= max_tokens (0 is a no-op); on the STREAM
+ *               path also ceil(T / 128) + E <= 65535 (TPM_ERR_SHAPE otherwise; AUTO
+ *               never streams that many).
  *   Y_dev       [T x d] of out_dtype.
  * Asynchronous on `stream`, allocates nothing; one handle on one stream at a time. */
 tpm_status tp_moe_fwd(tpm_moe_t h, const void *X_dev, const int32_t *counts_dev, int64_t T,

@@ -150,6 +150,9 @@ tpm_status tp_moe_fwd(tpm_moe_t handle, const void *X_dev, const int32_t *counts
   // kernel for more (both read and write the same hidden layout).
   const bool streamed =
       d.path == TPM_PATH_STREAM || (d.path == TPM_PATH_AUTO && T <= kGroupStreamRows * d.n_experts);
+  // the streaming launch takes one grid row per 128-token tile (+ one per expert)
+  if (streamed && (T + kGroupStreamRows - 1) / kGroupStreamRows + d.n_experts > 65535)
+    return TPM_ERR_SHAPE;
   hipError_t e = streamed
                      ? launch_group_stream(epi1, X_dev, d.d_model, T, d.d_model, h->w1, h->w1_stride,
                                            h->n1 / kFragN, counts_dev, g1.n_groups, h->hidden, 0, 0,
