@@ -120,11 +120,12 @@ def test_tiled_split_round_and_grouped_experts_in_graphs():
         sh.close()
     es = synth.ExpertSpec(d_model=1024, ffn_expert=512, n_experts=4)
     w1, w2 = es.weights()
-    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), max_tokens=400)
     counts = torch.tensor([100, 0, 257, 43], dtype=torch.int32, device=DEV)
     xe = synth.tokens(400, 1024).to(DEV)
     ye = torch.empty(400, 1024, device=DEV)
-    try:
-        check_graph("grouped experts", lambda: ge.forward(xe, counts, out=ye), [ye])
-    finally:
-        ge.close()
+    for path in ("stream", "tiled"):  # both grouped kernels (AUTO streams at this size)
+        ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), max_tokens=400, path=path)
+        try:
+            check_graph("grouped experts, " + path, lambda: ge.forward(xe, counts, out=ye), [ye])
+        finally:
+            ge.close()

@@ -91,6 +91,16 @@ def test_ragged_and_empty_groups(act, path):
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_one_expert_takes_every_token(path):
+    """All 500 tokens on the last expert: four row tiles of one expert (the last
+    holding 116 rows, its fourth 32-row block partly filled), the others empty."""
+    spec = synth.ExpertSpec(d_model=512, ffn_expert=256, n_experts=4)
+    counts = [0, 0, 0, 500]
+    x, w1, w2, (y,) = run(spec, counts, path=path)
+    check(x, counts, w1, w2, y)
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_sixteen_experts_bf16_out_and_deterministic(path):
     spec = synth.ExpertSpec(d_model=2048, ffn_expert=1024, n_experts=16)
     counts = synth.expert_counts(16)
