@@ -132,6 +132,34 @@ def test_full_size_expert_layer_sampled(path):
     check(x, counts, w1, w2, y, rows=synth.sample_rows(sum(counts), 48))
 
 
+def test_streaming_launch_at_its_grid_limit():
+    """The streaming path takes one grid row per 128-token tile plus one per expert:
+    8388352 tokens on one expert fill 65535 rows exactly (sampled rows against the
+    oracle); one token more is refused with TPM_ERR_SHAPE before any launch."""
+    spec = synth.ExpertSpec(d_model=64, ffn_expert=64, n_experts=1)
+    w1, w2 = spec.weights()
+    t_ok = 128 * 65534
+    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), max_tokens=t_ok + 1, path="stream")
+    try:
+        g = torch.Generator(device=DEV).manual_seed(4242)
+        x = torch.randn(t_ok + 1, 64, generator=g, device=DEV).to(torch.bfloat16)
+        say("streaming grid limit: tokens", t_ok)
+        y = ge.forward(x[:t_ok], torch.tensor([t_ok], dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        rows = synth.sample_rows(t_ok, 64)
+        ref = oracle.grouped_experts(x[rows].cpu(), [len(rows)], list(w1), list(w2), "silu_gate")
+        err = oracle.rel_err(y[rows].cpu(), ref)
+        say("err", err)
+        assert err <= TOL_BF16
+        del y
+        with pytest.raises(tpm.TpmError) as e:
+            ge.forward(x, torch.tensor([t_ok + 1], dtype=torch.int32, device=DEV))
+        assert e.value.status == 2  # TPM_ERR_SHAPE
+        torch.cuda.synchronize()
+    finally:
+        ge.close()
+
+
 def test_binding_refuses_mismatched_tokens_and_output():
     spec = synth.ExpertSpec(d_model=256, ffn_expert=128, n_experts=2)
     w1, w2 = spec.weights()
