@@ -36,7 +36,9 @@ def gpu_merge(vals, maxs, sums, out_dtype=torch.float32):
 
 
 @pytest.mark.parametrize("rows,dim,k", [(2048, 128, 8), (1, 8, 1), (3, 136, 2), (257, 64, 16),
-                                        (100, 512, 5)])
+                                        (100, 512, 5),
+                                        (4100, 1024, 3),    # more 8-value groups than the grid's cap: stride loop
+                                        (2, 1 << 20, 2)])   # the largest dim the call accepts
 def test_parity_fp32(rows, dim, k):
     vals, maxs, sums = synth.attn_partials(rows, dim, k, seed=rows + k)
     say("merge fp32 rows", rows, "dim", dim, "k", k)
