@@ -485,7 +485,10 @@ def tp_moe_destroy(handle: int) -> None:
 
 class GroupedExperts:
     """The experts held by one GPU as one grouped MLP.  w1: [E, d, 2F] (silu_gate:
-    gate then up columns) or [E, d, F]; w2: [E, F, d]; bf16 on the GPU."""
+    gate then up columns) or [E, d, F]; w2: [E, F, d]; bf16 on the GPU.  path:
+    "stream" (both projections stream each expert's weights once per 128 of its
+    tokens), "tiled" (256-token matrix-core tiles) or "auto" (stream when the
+    tokens number at most 128 per expert)."""
 
     def __init__(self, w1, w2, activation="silu_gate", max_tokens=8192, out_dtype=None,
                  path="auto", stream=None):
