@@ -852,7 +852,7 @@ def main():
                    "config": {"workload": "prefill shard: one TP=8 rank, d_model 8192, F 3584, "
                                           "SwiGLU, X [8192 x 8192] bf16"},
                    "roofline": {"bound": "mfma", "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "kernel": "k_tiled<SILU_GATE> (gate/up projection)",
+                                "kernel": "k_gemm<SILU_GATE> (gate/up projection)",
                                 "achieved": round(flops1 / (p1_ms * 1e-3) / 1e12, 1),
                                 "frac": round(flops1 / (p1_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                                 "avg_launch_us": round(p1_ms * 1e3, 1),
@@ -860,7 +860,7 @@ def main():
                                 "min_launch_us": round(min(p1) * 1e3, 1),
                                 "launches": len(p1), "warmup_calls": args.prefill_warmup,
                                 "traffic": stored_traffic("gate_up_prefill")},
-                   "down": {"kernel": "k_tiled<OUT_F32> (down projection)",
+                   "down": {"kernel": "k_gemm<OUT_F32> (down projection)",
                             "achieved_TFLOPs": round(flops2 / (p2_ms * 1e-3) / 1e12, 1),
                             "avg_launch_us": round(p2_ms * 1e3, 1)}}
         log("prefill: %.3f ms/call, %.1f TFLOP/s" % (t_call * 1e3, tf))

@@ -17,7 +17,7 @@ OBJ_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libtpmlp.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "api_proj.cpp", "api_moe.cpp", "k_pack.hip", "k_stream.hip", "k_tiled.hip", "k_group.hip", "k_f32.hip", "k_reduce.hip",
+SOURCES = ["api.cpp", "api_proj.cpp", "api_moe.cpp", "k_pack.hip", "k_stream.hip", "k_tiled.hip", "k_gemm.hip", "k_group.hip", "k_f32.hip", "k_reduce.hip",
            "k_quant.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.

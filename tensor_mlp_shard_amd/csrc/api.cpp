@@ -264,7 +264,7 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
     split.max_tiles = h->split_tiles;
   }
   if (path == TPM_PATH_TILED)
-    e = launch_tiled_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden, 0, 0,
+    e = launch_gemm(epi1, X_dev, d.d_model, M, d.d_model, h->w1, h->n1, h->hidden, 0, 0,
                           h->ks2, split, s, t1);
   if (e == hipSuccess) {
     if (path == TPM_PATH_STREAM)
@@ -272,7 +272,7 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
                              h->ks2, h->w2, h->n2 / kFragN, partial_dev, d.d_model, d.d_model, 0,
                              ws, s, t2);
     else
-      e = launch_tiled_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
+      e = launch_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
                             d.d_model, d.d_model, 0, split, s, t2);
   }
   return from_hip(e);

@@ -195,7 +195,7 @@ tpm_status tp_proj_fwd(tpm_proj_t handle, const void *X_dev, int64_t M, void *Y_
       split.n_cu = h->n_cu;
       split.max_tiles = h->split_tiles;
     }
-    e = launch_tiled_gemm(epi, X_dev, K, M, K, h->w, h->n_pad, Y_dev, N, N, 0, split, s);
+    e = launch_gemm(epi, X_dev, K, M, K, h->w, h->n_pad, Y_dev, N, N, 0, split, s);
   }
   return from_hip(e);
 }
