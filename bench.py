@@ -713,11 +713,27 @@ def run_attn_merge(tpm, synth, dev, reps=200):
                     "statistics; many calls per HIP graph, time per call"}
 
 
-def cpu_baseline(host_inputs, budget_s=12.0):
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def cpu_baseline(host_inputs, budget_s=12.0, prefill_rows=256):
     """The fp64 oracle on the host over whole decode steps (8 shards at M = 32 plus
-    the partials sum) until about `budget_s` seconds of oracle compute have run."""
+    the partials sum) until about `budget_s` seconds of oracle compute have run; then
+    the prefill shard (M = 8192) on a seeded sample of `prefill_rows` token rows,
+    scaled by M / rows (token rows are independent, so the cost is linear in M) and
+    labelled as extrapolated."""
     import numpy as np
     import oracle
+    from tensor_mlp_shard_amd import synth
     x, a_sh, b_sh = host_inputs
     X = oracle._f64(x)
     widened = [(oracle._f64(a), oracle._f64(b)) for a, b in zip(a_sh, b_sh)]
@@ -738,11 +754,26 @@ def cpu_baseline(host_inputs, budget_s=12.0):
     weight_bytes = sum(a.shape[0] * a.shape[1] * 2 + b.shape[0] * b.shape[1] * 2
                        for a, b in zip(a_sh, b_sh))
     per_step = t_total / steps_done
+    # prefill: rank 0's shard, the same seeded rows the prefill parity test samples
+    rows = synth.sample_rows(M_PREFILL, prefill_rows)
+    xp = synth.tokens(M_PREFILL)[rows]
+    _, t_rows = oracle.timed_shard_forward(oracle._f64(xp), widened[0][0], widened[0][1],
+                                           "silu_gate")
+    F = FFN // TP
+    flops_call = 2 * M_PREFILL * D_MODEL * 2 * F + 2 * M_PREFILL * F * D_MODEL
+    t_call = t_rows * M_PREFILL / len(rows)
     return {"value": round(weight_bytes / per_step / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "%d whole decode step(s): 8 TP=8 rank shards at M=32 + partials sum, "
                       "fp64, %.1f s of oracle compute" % (steps_done, t_total),
-            "s_per_step": round(per_step, 4)}
+            "s_per_step": round(per_step, 4),
+            "prefill": {"value": round(flops_call / t_call / 1e12, 6), "unit": "TFLOP/s",
+                        "kind": "oracle", "extrapolated": True,
+                        "rows_timed": len(rows), "seconds_timed": round(t_rows, 3),
+                        "s_per_call_extrapolated": round(t_call, 2),
+                        "sample": "prefill shard (rank 0 of TP=8, M=8192): %d seeded token rows "
+                                  "timed, scaled by M/rows (rows are independent, cost linear "
+                                  "in M)" % len(rows)}}
 
 
 def calib_copy(dev, nbytes=1 << 30, reps=3):
@@ -807,8 +838,9 @@ def main():
     ms_step_eager = elapsed_eager / args.steps * 1e3
 
     F = FFN // TP
-    k1_bytes = D_MODEL * 2 * F * 2 + M_DECODE * D_MODEL * 2 + M_DECODE * F * 2
-    k2_bytes = F * D_MODEL * 2 + M_DECODE * F * 2 + M_DECODE * D_MODEL * 4
+    # algorithmic bytes: the weights and X read once; the H round trip is not credited
+    k1_bytes = D_MODEL * 2 * F * 2 + M_DECODE * D_MODEL * 2
+    k2_bytes = F * D_MODEL * 2 + M_DECODE * D_MODEL * 4
     k1_ms = sum(k1) / len(k1)
     k2_ms = sum(k2) / len(k2)
     achieved = k1_bytes / (k1_ms * 1e-3) / 1e9

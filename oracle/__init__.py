@@ -81,6 +81,8 @@ def _load():
         lib.orc_partials_sum.argtypes = [ctypes.POINTER(dp), ctypes.c_int32,
                                          ctypes.c_int64, dp]
         lib.orc_partials_sum.restype = ctypes.c_int
+        lib.orc_matmul.argtypes = [dp, ctypes.c_int64, ctypes.c_int64, dp, ctypes.c_int64, dp]
+        lib.orc_matmul.restype = ctypes.c_int
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -205,7 +207,11 @@ def projection(x, w) -> np.ndarray:
     X, W = _f64(x), _f64(w)
     if X.ndim != 2 or W.ndim != 2 or X.shape[1] != W.shape[0]:
         raise ValueError("shapes %s and %s do not chain" % (X.shape, W.shape))
-    return X @ W
+    Y = np.zeros((X.shape[0], W.shape[1]), dtype=np.float64)
+    rc = _load().orc_matmul(_ptr(X), X.shape[0], X.shape[1], _ptr(W), W.shape[1], _ptr(Y))
+    if rc != 0:
+        raise RuntimeError("orc_matmul failed with code %d" % rc)
+    return Y
 
 
 def reduce_add_rmsnorm(partials, residual, gamma, eps: float):

@@ -116,6 +116,26 @@ int orc_partials_sum(const double *const *parts, int32_t k, int64_t numel, doubl
   return ORC_OK;
 }
 
+/* One projection Y [M x N] = X [M x K] W [K x N] (page "大模型推理系统揭秘（07）
+ * Multi-GPU", section 1.2.2: Y = XW, split by columns or by rows of W).  Plain loops:
+ * Y[m][n] = sum_k X[m][k] * W[k][n], summed over k in ascending order; rows over threads. */
+int orc_matmul(const double *X, int64_t M, int64_t K, const double *W, int64_t N, double *Y) {
+  if (M < 0 || K < 1 || N < 1) return ORC_BAD_ARG;
+  if (M == 0) return ORC_OK;
+  if (!X || !W || !Y) return ORC_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m) {
+    double *yrow = Y + m * N;
+    for (int64_t n = 0; n < N; ++n) yrow[n] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double x = X[m * K + k];
+      const double *wrow = W + k * N;
+      for (int64_t n = 0; n < N; ++n) yrow[n] += x * wrow[n];
+    }
+  }
+  return ORC_OK;
+}
+
 int orc_num_threads(void) {
   int n = 1;
 #ifdef _OPENMP

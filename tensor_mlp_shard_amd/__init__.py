@@ -514,7 +514,7 @@ class GroupedExperts:
         if counts.dtype != torch.int32 or counts.numel() != self.n_experts:
             raise ValueError("counts must be int32 [%d]" % self.n_experts)
         if out is None:
-            out = torch.empty((T, self.d_model), dtype=self.out_dtype, device=x.device)
+            out = torch.zeros((T, self.d_model), dtype=self.out_dtype, device=x.device)
         elif tuple(out.shape) != (T, self.d_model) or out.dtype != self.out_dtype:
             raise ValueError("out must be [%d, %d] of %s" % (T, self.d_model, self.out_dtype))
         tp_moe_fwd(self.handle, x, counts, T, out, stream)

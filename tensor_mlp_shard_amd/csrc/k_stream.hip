@@ -22,6 +22,12 @@
 //    halves read 64 contiguous bytes of a row per k-step pair, see the fragment
 //    order in tpm_internal.h) for the first product, the packed hidden buffer
 //    (1 KiB contiguous per wave load) for the second.
+//  * A few tokens (at most 16): only the 8 or 16 token rows that exist are loaded
+//    per batch instead of the tile's 32, and fragment lanes of rows past M read
+//    row M - 1 (products never stored); for the packed hidden operand those lanes
+//    load row M - 1's piece, so a fragment load touches only existing rows' lines.
+//    The token share of the per-CU load traffic drops 4x at M <= 8 (70B-class TP=8
+//    shard: 35.1 -> 33.6 us at M = 8, 37.3 -> 34.5 us at M = 1).
 //  * The waves' accumulators are summed in LDS in wave order, then the epilogue
 //    runs: SiLU(gate) * up, tanh or identity, written as bf16 into the packed
 //    hidden buffer, or the partial store.
@@ -97,7 +103,7 @@ __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (
 // arrival counter; the last to arrive adds the S slices in slice order (so the
 // result does not depend on arrival order), runs the epilogue and resets the
 // counter to zero for the next call.  Nothing ever waits for another workgroup.
-template <int EPI, int MT, int C, int NW>
+template <int EPI, int MT, int C, int NW, int TRQ>
 __global__ void __launch_bounds__(NW * 64)
 k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
          const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
@@ -115,6 +121,9 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   constexpr int RBYTES = NW * 16 * 64 * 4;
   constexpr int SBYTES = XBYTES > RBYTES ? XBYTES : RBYTES;
   static_assert(!FIRST || PB == 2, "token staging assumes 128-byte row segments");
+  // TRQ < 4 (at most 8 TRQ tokens, one token tile): only the first 8 TRQ rows of the
+  // tile are loaded; fragment lanes of rows past M read row M - 1 (never stored).
+  static_assert(TRQ == 4 || (MT == 1 && (TRQ == 1 || TRQ == 2)), "token row groups");
 
   __shared__ __attribute__((aligned(16))) char smem[SBYTES];  // token staging, then reduction
   __shared__ float vsum[16][64];
@@ -142,24 +151,29 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   const int wb_hi = b_lo + (b_hi - b_lo) * (wave + 1) / NW;
   const int nb = wb_hi - wb_lo;
 
+  const int trow = TRQ < 4 ? min(lane & 31, M - 1) : (lane & 31);  // staged row a fragment lane reads
+
   // Weight fragments of block C u + c at k-step s: wp[(s * n_cb + c) * 64].
   const int n_cb = n_units * C;
   const u32x4_t *wp = W + static_cast<int64_t>(u) * C * 64 + lane;
   // Token operand.  FIRST: row-major X; lane l loads 16 bytes of row 8 j + l / 8 of
   // the batch's 128-byte segment, chunk l % 8.  Otherwise: packed H fragments.
   const u32x4_t *ap[MT];
-  const uint16_t *xrow[MT * 4];
+  const uint16_t *xrow[MT * TRQ];
   if constexpr (FIRST) {
 #pragma unroll
-    for (int j = 0; j < MT * 4; ++j) {
+    for (int j = 0; j < MT * TRQ; ++j) {
       int row = 32 * mt0 + 8 * j + (lane >> 3);
       row = row < M ? row : M - 1;  // rows >= M repeat the last row; never stored as output
       xrow[j] = A + static_cast<int64_t>(row) * lda + 8 * (lane & 7);
     }
   } else {
+    // TRQ < 4: lanes of rows past M load row M - 1's piece, so a fragment load
+    // touches only the cache lines of the rows that exist
+    const int alane = TRQ < 4 ? (lane & 32) + min(lane & 31, M - 1) : lane;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
-      ap[m] = reinterpret_cast<const u32x4_t *>(A) + static_cast<int64_t>(mt0 + m) * ks * 64 + lane;
+      ap[m] = reinterpret_cast<const u32x4_t *>(A) + static_cast<int64_t>(mt0 + m) * ks * 64 + alane;
   }
   uint16_t *xs = reinterpret_cast<uint16_t *>(smem) + wave * XWAVE;
 
@@ -171,10 +185,10 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][c][r] = 0.0f;
 
-  if (nb > 0) {
+  {
     // One batch in registers: weight fragments and the token operand (FIRST: the
     // raw 16-byte pieces of the staged rows; otherwise fragments).
-    constexpr int NA = FIRST ? MT * 4 : D * MT;
+    constexpr int NA = FIRST ? MT * TRQ : D * MT;
     u32x4_t w0[D][C], a0[NA], w1[D][C], a1[NA];
     auto load = [&](u32x4_t (&wb)[D][C], u32x4_t (&ab)[NA], int b) {
       const int p0 = PB * min(wb_lo + b, wb_hi - 1);  // first pair of the batch
@@ -185,7 +199,7 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
           wb[i][c] = __builtin_nontemporal_load(&wp[(static_cast<int64_t>(2 * p0 + i) * n_cb + c) * 64]);
       if constexpr (FIRST) {
 #pragma unroll
-        for (int j = 0; j < MT * 4; ++j)
+        for (int j = 0; j < MT * TRQ; ++j)
           ab[j] = *reinterpret_cast<const u32x4_t *>(xrow[j] + 32 * p0);
       } else {
 #pragma unroll
@@ -198,14 +212,14 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
       u32x4_t frag[D][MT];
       if constexpr (FIRST) {
 #pragma unroll
-        for (int j = 0; j < MT * 4; ++j)
+        for (int j = 0; j < MT * TRQ; ++j)
           *reinterpret_cast<u32x4_t *>(&xs[(8 * j + (lane >> 3)) * XROW + 8 * (lane & 7)]) = ab[j];
 #pragma unroll
         for (int i = 0; i < D; ++i)
 #pragma unroll
           for (int m = 0; m < MT; ++m)
             frag[i][m] = *reinterpret_cast<const u32x4_t *>(
-                &xs[(32 * m + (lane & 31)) * XROW + 32 * (i >> 1) + 16 * (lane >> 5) + 8 * (i & 1)]);
+                &xs[(32 * m + trow) * XROW + 32 * (i >> 1) + 16 * (lane >> 5) + 8 * (i & 1)]);
       } else {
 #pragma unroll
         for (int i = 0; i < D; ++i)
@@ -224,7 +238,7 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
         }
       }
     };
-    load(w0, a0, 0);
+    if (nb > 0) load(w0, a0, 0);
     // The scheduling barriers keep each batch's loads ahead of the previous batch's
     // products, so the products wait only for their own batch.
     for (int b = 0; b < nb; b += 2) {
@@ -330,12 +344,12 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
 // waves then get only 14 k-steps each: +14%; 4: +6%).
 constexpr int stream_waves(bool first, int S) { return first && S == 1 ? 4 : 8; }
 
-template <int EPI, int MT, int C, int NW>
+template <int EPI, int MT, int C, int NW, int TRQ = 4>
 hipError_t launch_stream_nw(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
                             int64_t n_units, int64_t blocks, int S, void *out, int64_t ldo,
                             int64_t n_store, int64_t ks_out, float *scratch, int *counters,
                             hipStream_t s, const Timing &t) {
-  hipExtLaunchKernelGGL((k_stream<EPI, MT, C, NW>), dim3(static_cast<unsigned>(blocks)),
+  hipExtLaunchKernelGGL((k_stream<EPI, MT, C, NW, TRQ>), dim3(static_cast<unsigned>(blocks)),
                         dim3(NW * 64), 0, s, t.start, t.stop, 0, static_cast<const uint16_t *>(A),
                         lda, static_cast<int>(M), static_cast<int>(ks),
                         static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
@@ -359,6 +373,24 @@ hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, 
     return hipErrorInvalidConfiguration;
   float *scratch = ws.buf;
   int *counters = ws.cnt;
+  if constexpr (MT == 1 && C == 1) {
+    constexpr bool first = tokens_row_major(EPI);
+    // a few tokens: load only the token rows that exist (8 or 16 of the tile's 32)
+    if (M <= 16) {
+      if (stream_waves(first, S) == 4) {
+        if (M <= 8)
+          return launch_stream_nw<EPI, MT, C, 4, 1>(A, lda, M, ks, W, n_units, blocks, S, out,
+                                                           ldo, n_store, ks_out, scratch, counters, s, t);
+        return launch_stream_nw<EPI, MT, C, 4, 2>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
+                                                         n_store, ks_out, scratch, counters, s, t);
+      }
+      if (M <= 8)
+        return launch_stream_nw<EPI, MT, C, 8, 1>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
+                                                         n_store, ks_out, scratch, counters, s, t);
+      return launch_stream_nw<EPI, MT, C, 8, 2>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
+                                                       n_store, ks_out, scratch, counters, s, t);
+    }
+  }
   if (stream_waves(tokens_row_major(EPI), S) == 4)
     return launch_stream_nw<EPI, MT, C, 4>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
                                            ks_out, scratch, counters, s, t);

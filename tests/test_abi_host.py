@@ -277,3 +277,36 @@ def test_attn_merge_validation(lib):
     assert f(v, m, e, 2, 4, 16, 0, ctypes.c_void_p(0x1000), 1, None, None, None) == INVALID
     # rows = 0 is a no-op that never touches the device
     assert f(v, m, e, 2, 0, 16, 0, out, 0, mo, eo, None) == OK
+
+
+HIP_ERR = 4  # TPM_ERR_HIP
+
+
+def _no_device():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_device(), reason="the HIP error path is forced by having no device")
+def test_create_without_a_device_reports_hip_error(lib):
+    """With no GPU, the first HIP call of each create (hipGetDevice) fails: the call
+    returns TPM_ERR_HIP, clears *out and leaves nothing allocated; no kernel is
+    launched since the failure comes before any allocation."""
+    h = ctypes.c_void_p(1234)
+    d = desc(d_model=64, ffn_shard=128, max_tokens=8)
+    assert lib.tp_mlp_shard_create(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                                   ctypes.c_void_p(0x2000), None, ctypes.byref(h)) == HIP_ERR
+    assert h.value is None
+    pd = tpm.TpmProjDesc(64, 64, 8, tpm.BF16, tpm.F32, 0, 0)
+    h = ctypes.c_void_p(1234)
+    assert lib.tp_proj_create(ctypes.byref(pd), ctypes.c_void_p(0x1000), None,
+                              ctypes.byref(h)) == HIP_ERR
+    assert h.value is None
+    md = tpm.TpmMoeDesc(512, 256, 4, 64, 1, tpm.BF16, tpm.F32, 0)
+    h = ctypes.c_void_p(1234)
+    assert lib.tp_moe_create(ctypes.byref(md), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                             None, ctypes.byref(h)) == HIP_ERR
+    assert h.value is None

@@ -77,14 +77,15 @@ def test_reduce_fp8(k, out_dtype):
 
 
 def test_fp8_pipeline_after_mlp_shards_and_determinism():
-    """Eight TP shards of a small SwiGLU MLP, partials through FP8, summed: close to
-    the unsplit MLP, and bitwise repeatable."""
+    """Eight TP shards of a small SwiGLU MLP, partials through FP8, summed: bitwise
+    repeatable, and element by element within the E4M3 rounding bound of the partials
+    plus the bf16 path's own bound against the unsplit MLP."""
     from tensor_mlp_shard_amd import synth
     a_sh, b_sh = synth.ModelSpec(d_model=1024, ffn=4096).shards(8)
     x = synth.tokens(32, d=1024)
     Z = []
     for rep in range(2):
-        qs, ss = [], []
+        qs, ss, ps = [], [], []
         for a, b in zip(a_sh, b_sh):
             sh = tpm.Shard(a.to(DEV), b.to(DEV), "silu_gate", max_tokens=32)
             p = sh.forward(x.to(DEV))
@@ -95,14 +96,21 @@ def test_fp8_pipeline_after_mlp_shards_and_determinism():
             sh.close()
             qs.append(q)
             ss.append(s)
+            ps.append(p.cpu())
         z = torch.empty(32, 1024, device=DEV)
         tpm.tp_partials_reduce_fp8(qs, ss, z)
         torch.cuda.synchronize()
         Z.append(z.cpu())
     assert torch.equal(Z[0], Z[1])
     ref = oracle.unsplit_output(x, a_sh, b_sh, "silu_gate")
-    err = oracle.rel_err(Z[0], ref)
-    say("fp8 partials, 8 shards: err vs unsplit", err)
-    # E4M3 keeps 3 mantissa bits: a few percent of the RMS, far from the bf16 bound of
-    # the exact path but within the format's reach
-    assert err < 0.3
+    rms = float((ref ** 2).mean() ** 0.5)
+    # the exact (fp32-partial) path is within the bf16 bound of the unsplit MLP ...
+    exact_gpu = oracle.partials_sum(ps)
+    assert oracle.rel_err(exact_gpu, ref) <= 2e-2
+    # ... and FP8 transport adds at most half a grid spacing per partial element (2^-4
+    # of the magnitude, 2^-10 scale units near 0), so element by element
+    bound = sum(p.double().numpy().__abs__() * 2.0 ** -4 + 2.0 ** -10 * s.cpu().double().numpy()[:, None]
+                for p, s in zip(ps, ss))
+    got = Z[0].double().numpy()
+    assert (abs(got - ref) <= bound + 2e-2 * rms).all()
+    say("fp8 partials, 8 shards: err vs unsplit", oracle.rel_err(Z[0], ref))

@@ -123,6 +123,25 @@ def test_counts_past_the_rows_are_clamped_and_rows_past_the_counts_untouched(pat
 
 
 @pytest.mark.parametrize("path", PATHS)
+def test_default_out_is_zero_past_the_counts(path):
+    # no out given and counts summing to less than T: the binding's own output buffer
+    # starts at zero, so rows no expert owns come back as zeros (never stale memory)
+    spec = synth.ExpertSpec(d_model=256, ffn_expert=128, n_experts=4)
+    w1, w2 = spec.weights("silu_gate")
+    x = synth.tokens(40, d=spec.d_model, seed=5)
+    ge = tpm.GroupedExperts(w1.to(DEV), w2.to(DEV), "silu_gate", max_tokens=40, path=path)
+    try:
+        torch.empty(40 * 256 * 4, dtype=torch.float32, device=DEV).fill_(7.0)  # dirty the pool
+        y = ge.forward(x.to(DEV), torch.tensor([10, 0, 5, 0], dtype=torch.int32, device=DEV))
+        torch.cuda.synchronize()
+        y = y.cpu()
+    finally:
+        ge.close()
+    check(x, [10, 0, 5, 0], w1, w2, y)
+    assert torch.all(y[15:] == 0.0)
+
+
+@pytest.mark.parametrize("path", PATHS)
 def test_full_size_expert_layer_sampled(path):
     """The 16 experts of one GPU at the 70B-class width (d 8192, expert width 2048)."""
     spec = synth.ExpertSpec()

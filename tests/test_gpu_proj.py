@@ -63,7 +63,7 @@ def test_stream_forced_many_token_groups_narrow_projection():
     w = (torch.randn(8192, 256, generator=g) * 0.02).to(torch.bfloat16)
     p = tpm.Projection(w.to(DEV), max_tokens=200, out_dtype=torch.float32, path="stream")
     try:
-        for M in (32, 200, 96, 32):
+        for M in (32, 8, 200, 1, 96, 32):
             x = synth.tokens(M)
             say("forced stream, narrow projection M", M)
             y = p.forward(x.to(DEV)).cpu()
