@@ -149,6 +149,26 @@ tpm_status tp_mlp_shard_create(const tpm_desc *desc, const void *A_dev, const vo
 tpm_status tp_mlp_shard_fwd(tpm_shard_t h, const void *X_dev, int64_t M, void *partial_dev,
                             void *stream);
 
+/* For callers that cannot allocate device memory at all (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as tp_mlp_shard_fwd on the decode (weight-streaming) path, 1 <= M <= 64
+ * (M = 0 is a successful no-op), bf16 handles only, with the hidden buffer and the
+ * contraction-slice scratch in one array of TPM_NOALLOC_SCRATCH_BYTES that the
+ * library holds per device from load to process end, instead of the handle's
+ * workspace (so a handle created with max_tokens = 0 works too).  Its arguments,
+ * layouts and results are those of tp_mlp_shard_fwd; the two return the same
+ * partial bit for bit.  Allocates nothing, calls no allocating routine.
+ *
+ * Errors: TPM_ERR_SHAPE for M > 64, a non-bf16 handle or a shard whose scratch need
+ * (ceil(M / 32) * ffn_padded / 16 KiB of hidden rows, plus slice sums for narrow
+ * shards) exceeds TPM_NOALLOC_SCRATCH_BYTES; TPM_ERR_HIP if the array's device
+ * address cannot be obtained (first call on a device).  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams, or a handle
+ * used from two threads) race. */
+#define TPM_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+tpm_status tp_mlp_shard_fwd_noalloc(tpm_shard_t h, const void *X_dev, int64_t M,
+                                    void *partial_dev, void *stream);
+
 /* Sum k partials held on this GPU, in rank order, with fp32 accumulation:
  *   out_dev[e] = (((p_0[e] + p_1[e]) + p_2[e]) + ...) + p_{k-1}[e],  0 <= e < numel.
  *

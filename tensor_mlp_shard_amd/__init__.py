@@ -27,7 +27,8 @@ import ctypes
 import os
 
 __all__ = [
-    "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_destroy",
+    "tp_mlp_shard_plan", "tp_mlp_shard_create", "tp_mlp_shard_fwd", "tp_mlp_shard_fwd_noalloc",
+    "tp_mlp_shard_destroy",
     "tp_partials_reduce", "tp_partials_reduce_add_rmsnorm", "tp_partials_quantize_fp8",
     "tp_partials_reduce_fp8", "tp_attn_partials_merge", "attn_partials_merge", "tp_proj_create", "tp_proj_fwd", "tp_proj_destroy",
     "Projection", "tp_moe_create", "tp_moe_fwd", "tp_moe_destroy", "GroupedExperts",
@@ -100,6 +101,8 @@ def capi():
     lib.tp_mlp_shard_create.restype = ctypes.c_int
     lib.tp_mlp_shard_fwd.argtypes = [vp, vp, i64, vp, vp]
     lib.tp_mlp_shard_fwd.restype = ctypes.c_int
+    lib.tp_mlp_shard_fwd_noalloc.argtypes = [vp, vp, i64, vp, vp]
+    lib.tp_mlp_shard_fwd_noalloc.restype = ctypes.c_int
     lib.tp_partials_reduce.argtypes = [ctypes.POINTER(vp), i32, i64, i32, vp, i32, vp]
     lib.tp_partials_reduce.restype = ctypes.c_int
     lib.tp_partials_reduce_add_rmsnorm.argtypes = [ctypes.POINTER(vp), i32, i64, i64, i32, vp, vp,
@@ -196,6 +199,14 @@ def tp_mlp_shard_fwd(handle: int, X, M: int, partial, stream=None) -> None:
     _check(capi().tp_mlp_shard_fwd(ctypes.c_void_p(handle), _dev_ptr(X, "X"), int(M),
                                    _dev_ptr(partial, "partial"), _stream_ptr(stream)),
            "tp_mlp_shard_fwd")
+
+
+def tp_mlp_shard_fwd_noalloc(handle: int, X, M: int, partial, stream=None) -> None:
+    """The decode-path forward with the library's per-device scratch array instead of
+    the handle's workspace (1 <= M <= 64, bf16 handles; allocates nothing)."""
+    _check(capi().tp_mlp_shard_fwd_noalloc(ctypes.c_void_p(handle), _dev_ptr(X, "X"), int(M),
+                                           _dev_ptr(partial, "partial"), _stream_ptr(stream)),
+           "tp_mlp_shard_fwd_noalloc")
 
 
 def tp_partials_reduce(partials, out, stream=None) -> None:

@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "tpm_internal.h"
@@ -45,6 +46,32 @@ tpm_status from_hip(hipError_t e) {
   if (e == hipSuccess) return TPM_OK;
   if (e == hipErrorOutOfMemory) return TPM_ERR_OOM;
   return TPM_ERR_HIP;
+}
+
+// Scratch of tp_mlp_shard_fwd_noalloc: one array per device, held from module load
+// to process end.  In host code `scratch` only names the symbol; its device address
+// comes from hipGetSymbolAddress (per device, at the first call there) and only that
+// address is ever passed to kernels.
+constexpr int64_t kNoAllocScratchBytes = TPM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+tpm_status scratch_address(int dev, void **out) {
+  if (dev < 0 || dev >= kMaxDevices) return TPM_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return TPM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TPM_OK;
 }
 
 }  // namespace
@@ -275,6 +302,58 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
       e = launch_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
                             d.d_model, d.d_model, 0, split, s, t2);
   }
+  return from_hip(e);
+}
+
+tpm_status tp_mlp_shard_fwd_noalloc(tpm_shard_t handle, const void *X_dev, int64_t M,
+                                    void *partial_dev, void *stream) {
+  Shard *h = reinterpret_cast<Shard *>(handle);
+  if (!h) return TPM_ERR_INVALID_ARG;
+  const tpm_desc &d = h->desc;
+  if (d.in_dtype != TPM_BF16 || M < 0 || M > kStreamMaxTokens) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X_dev || !partial_dev) return TPM_ERR_INVALID_ARG;
+  if (!aligned(X_dev) || !aligned(partial_dev)) return TPM_ERR_ALIGN;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != h->device) return TPM_ERR_INVALID_ARG;
+
+  // Carve the scratch: the packed hidden rows of the token tiles, then the
+  // contraction slices' sums and arrival counters (the larger need of the two
+  // products, which run one after the other).
+  const StreamPlan p1 = stream_plan(M, h->n1 / kFragN, h->ks1);
+  const StreamPlan p2 = stream_plan(M, h->n2 / kFragN, h->ks2);
+  const int64_t hidden_bytes = (M + 31) / 32 * h->ks2 * 1024;
+  const int64_t f1 = p1.s > 1 ? (h->n1 / kFragN) * p1.s * p1.mt * 1024 : 0;
+  const int64_t f2 = p2.s > 1 ? (h->n2 / kFragN) * p2.s * p2.mt * 1024 : 0;
+  const int64_t c1 = p1.s > 1 ? h->n1 / kFragN / p1.c : 0;
+  const int64_t c2 = p2.s > 1 ? h->n2 / kFragN / p2.c : 0;
+  const int64_t floats = f1 > f2 ? f1 : f2;
+  const int64_t n_cnt = c1 > c2 ? c1 : c2;
+  const int64_t o_sk = round_up(hidden_bytes, kSubAlign);
+  const int64_t o_cnt = round_up(o_sk + floats * 4, kSubAlign);
+  const int64_t need = o_cnt + n_cnt * 4;
+  if (need > kNoAllocScratchBytes) return TPM_ERR_SHAPE;
+  void *base = nullptr;
+  const tpm_status st = scratch_address(dev, &base);
+  if (st != TPM_OK) return st;
+  char *b = static_cast<char *>(base);
+  StreamScratch ws;
+  ws.buf = floats ? reinterpret_cast<float *>(b + o_sk) : nullptr;
+  ws.cnt = n_cnt ? reinterpret_cast<int *>(b + o_cnt) : nullptr;
+  ws.floats = floats;
+  ws.n_counters = n_cnt;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int epi1 = first_epi(d.act);
+  const int epi2 = d.out_dtype == TPM_F32 ? EPI_OUT_F32 : EPI_OUT_BF16;
+  // the arrival counters must start at zero (a fill kernel, so a caller may capture it)
+  hipError_t e = n_cnt ? launch_zero_i32(ws.cnt, n_cnt, s) : hipSuccess;
+  if (e == hipSuccess)
+    e = launch_stream_gemm(epi1, p1, X_dev, d.d_model, M, h->ks1, h->w1, h->n1 / kFragN, b, 0, 0,
+                           h->ks2, ws, s);
+  if (e == hipSuccess)
+    e = launch_stream_gemm(epi2, p2, b, 0, M, h->ks2, h->w2, h->n2 / kFragN, partial_dev,
+                           d.d_model, d.d_model, 0, ws, s);
   return from_hip(e);
 }
 
