@@ -280,9 +280,17 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
   ws.cnt = h->counters;
   ws.floats = h->scratch_floats;
   ws.n_counters = h->n_counters;
+  // decode path: the second product may add two contraction halves atomically into
+  // the partial, which the first product then clears as a side job
+  const StreamPlan p2 = stream_plan_out(M, h->n2 / kFragN, h->ks2, d.out_dtype == TPM_F32);
+  StreamZero zero;
+  if (p2.atom) {
+    zero.out = static_cast<float *>(partial_dev);
+    zero.n = M * d.d_model;
+  }
   if (path == TPM_PATH_STREAM)
     e = launch_stream_gemm(epi1, stream_plan(M, h->n1 / kFragN, h->ks1), X_dev, d.d_model, M,
-                           h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, ws, s, t1);
+                           h->ks1, h->w1, h->n1 / kFragN, h->hidden, 0, 0, h->ks2, ws, s, t1, zero);
   TiledSplit split;
   if (h->scratch && h->counters && h->split_tiles > 0) {
     split.buf = h->scratch;
@@ -295,9 +303,8 @@ tpm_status tp_mlp_shard_fwd(tpm_shard_t handle, const void *X_dev, int64_t M, vo
                           h->ks2, split, s, t1);
   if (e == hipSuccess) {
     if (path == TPM_PATH_STREAM)
-      e = launch_stream_gemm(epi2, stream_plan(M, h->n2 / kFragN, h->ks2), h->hidden, 0, M,
-                             h->ks2, h->w2, h->n2 / kFragN, partial_dev, d.d_model, d.d_model, 0,
-                             ws, s, t2);
+      e = launch_stream_gemm(epi2, p2, h->hidden, 0, M, h->ks2, h->w2, h->n2 / kFragN, partial_dev,
+                             d.d_model, d.d_model, 0, ws, s, t2);
     else
       e = launch_gemm(epi2, h->hidden, 0, M, h->ffn_pad, h->w2, h->n2, partial_dev,
                             d.d_model, d.d_model, 0, split, s, t2);
@@ -321,12 +328,12 @@ tpm_status tp_mlp_shard_fwd_noalloc(tpm_shard_t handle, const void *X_dev, int64
   // contraction slices' sums and arrival counters (the larger need of the two
   // products, which run one after the other).
   const StreamPlan p1 = stream_plan(M, h->n1 / kFragN, h->ks1);
-  const StreamPlan p2 = stream_plan(M, h->n2 / kFragN, h->ks2);
+  const StreamPlan p2 = stream_plan_out(M, h->n2 / kFragN, h->ks2, d.out_dtype == TPM_F32);
   const int64_t hidden_bytes = (M + 31) / 32 * h->ks2 * 1024;
   const int64_t f1 = p1.s > 1 ? (h->n1 / kFragN) * p1.s * p1.mt * 1024 : 0;
-  const int64_t f2 = p2.s > 1 ? (h->n2 / kFragN) * p2.s * p2.mt * 1024 : 0;
+  const int64_t f2 = p2.s > 1 && !p2.atom ? (h->n2 / kFragN) * p2.s * p2.mt * 1024 : 0;
   const int64_t c1 = p1.s > 1 ? h->n1 / kFragN / p1.c : 0;
-  const int64_t c2 = p2.s > 1 ? h->n2 / kFragN / p2.c : 0;
+  const int64_t c2 = p2.s > 1 && !p2.atom ? h->n2 / kFragN / p2.c : 0;
   const int64_t floats = f1 > f2 ? f1 : f2;
   const int64_t n_cnt = c1 > c2 ? c1 : c2;
   const int64_t o_sk = round_up(hidden_bytes, kSubAlign);
@@ -348,9 +355,14 @@ tpm_status tp_mlp_shard_fwd_noalloc(tpm_shard_t handle, const void *X_dev, int64
   const int epi2 = d.out_dtype == TPM_F32 ? EPI_OUT_F32 : EPI_OUT_BF16;
   // the arrival counters must start at zero (a fill kernel, so a caller may capture it)
   hipError_t e = n_cnt ? launch_zero_i32(ws.cnt, n_cnt, s) : hipSuccess;
+  StreamZero zero;
+  if (p2.atom) {
+    zero.out = static_cast<float *>(partial_dev);
+    zero.n = M * d.d_model;
+  }
   if (e == hipSuccess)
     e = launch_stream_gemm(epi1, p1, X_dev, d.d_model, M, h->ks1, h->w1, h->n1 / kFragN, b, 0, 0,
-                           h->ks2, ws, s);
+                           h->ks2, ws, s, Timing(), zero);
   if (e == hipSuccess)
     e = launch_stream_gemm(epi2, p2, b, 0, M, h->ks2, h->w2, h->n2 / kFragN, partial_dev,
                            d.d_model, d.d_model, 0, ws, s);

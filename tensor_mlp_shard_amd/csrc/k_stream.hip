@@ -28,6 +28,13 @@
 //    load row M - 1's piece, so a fragment load touches only existing rows' lines.
 //    The token share of the per-CU load traffic drops 4x at M <= 8 (70B-class TP=8
 //    shard: 35.1 -> 33.6 us at M = 8, 37.3 -> 34.5 us at M = 1).
+//  * The second product with an fp32 output (stream_plan_out): two column blocks per
+//    workgroup over half the contraction each, so a workgroup loads the hidden
+//    operand of its half once for both blocks; the two halves are added into the
+//    output, which the first product clears as a side job.  With exactly two
+//    addends onto zero the result is the same in either arrival order.  4 waves
+//    (8 would give each wave only 14 k-steps of the 3584-deep shard: 14.8 us); 70B
+//    TP=8 decode shard: 13.0 -> 12.6 us.
 //  * The waves' accumulators are summed in LDS in wave order, then the epilogue
 //    runs: SiLU(gate) * up, tanh or identity, written as bf16 into the packed
 //    hidden buffer, or the partial store.
@@ -103,11 +110,12 @@ __device__ __forceinline__ void stream_epilogue(const float (*v)[64], uint16_t (
 // arrival counter; the last to arrive adds the S slices in slice order (so the
 // result does not depend on arrival order), runs the epilogue and resets the
 // counter to zero for the next call.  Nothing ever waits for another workgroup.
-template <int EPI, int MT, int C, int NW, int TRQ>
+template <int EPI, int MT, int C, int NW, int TRQ, bool ATOM>
 __global__ void __launch_bounds__(NW * 64)
 k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
          const u32x4_t *__restrict__ W, int n_units, int S, void *__restrict__ out, int64_t ldo,
-         int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters) {
+         int n_store, int ks_out, float *__restrict__ scratch, int *__restrict__ counters,
+         float *__restrict__ zero_out, int64_t zero_n) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
   constexpr int D = StreamShape<MT, C>::template depth<FIRST>;
   constexpr int PB = D / 2;  // k-step pairs per batch
@@ -124,6 +132,7 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   // TRQ < 4 (at most 8 TRQ tokens, one token tile): only the first 8 TRQ rows of the
   // tile are loaded; fragment lanes of rows past M read row M - 1 (never stored).
   static_assert(TRQ == 4 || (MT == 1 && (TRQ == 1 || TRQ == 2)), "token row groups");
+  static_assert(!ATOM || EPI == EPI_OUT_F32, "atomic slices add fp32 partials");
 
   __shared__ __attribute__((aligned(16))) char smem[SBYTES];  // token staging, then reduction
   __shared__ float vsum[16][64];
@@ -138,6 +147,17 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   const int sl = (blockIdx.x / n_units) % S;
   const int z = blockIdx.x / (n_units * S);
   const int mt0 = z * MT;  // first 32-row token tile of this workgroup
+
+  // Side job of a first product whose second product adds its contraction halves
+  // atomically: clear that product's fp32 output (16-byte stores, a contiguous share
+  // per workgroup).  The next launch on the stream sees the zeros.
+  if (zero_out) {
+    const int64_t n4 = zero_n >> 2;
+    const int64_t per = (n4 + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = per * blockIdx.x, hi = min(lo + per, n4);
+    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = lo + tid; i < hi; i += NT) reinterpret_cast<f32x4_t *>(zero_out)[i] = z;
+  }
 
   // Batches of this wave.  The contraction is cut into batches of PB k-step pairs
   // (ks is a multiple of 4, so the count is exact); slice sl takes a contiguous run
@@ -270,19 +290,27 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
         float a = red[0][e >> 6][e & 63];
 #pragma unroll
         for (int w = 1; w < NW; ++w) a += red[w][e >> 6][e & 63];
-        if (S == 1)
+        if constexpr (ATOM) {
+          // the two contraction halves meet in the zeroed output: 0 + a + b is the
+          // same in either arrival order, so the sum is deterministic
+          const int row = 32 * (mt0 + m) + mfma32_row(e >> 6, e & 63);
+          const int col = 32 * (C * u + c) + (e & 31);
+          if (row < M && col < n_store)
+            __hip_atomic_fetch_add(static_cast<float *>(out) + static_cast<int64_t>(row) * ldo + col, a,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (S == 1)
           vsum[e >> 6][e & 63] = a;
         else  // write-through store: complete at the device coherence point when counted
           __hip_atomic_store(&scratch[((wg_slot + sl) * BLK + m * C + c) * 1024 + e], a,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (S == 1) {
+      if (!ATOM && S == 1) {
         __syncthreads();
         stream_epilogue<EPI, NT>(vsum, hb, tid, mt0 + m, C * u + c, M, out, ldo, n_store, ks_out);
       }
     }
   }
-  if (S == 1) return;
+  if (ATOM || S == 1) return;
 
   // Arrival.  Every thread waits until its write-through stores have completed,
   // then one thread counts the workgroup in.  The scratch traffic never touches a
@@ -344,28 +372,35 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
 // waves then get only 14 k-steps each: +14%; 4: +6%).
 constexpr int stream_waves(bool first, int S) { return first && S == 1 ? 4 : 8; }
 
-template <int EPI, int MT, int C, int NW, int TRQ = 4>
+template <int EPI, int MT, int C, int NW, int TRQ = 4, bool ATOM = false>
 hipError_t launch_stream_nw(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
                             int64_t n_units, int64_t blocks, int S, void *out, int64_t ldo,
                             int64_t n_store, int64_t ks_out, float *scratch, int *counters,
-                            hipStream_t s, const Timing &t) {
-  hipExtLaunchKernelGGL((k_stream<EPI, MT, C, NW, TRQ>), dim3(static_cast<unsigned>(blocks)),
+                            hipStream_t s, const Timing &t, const StreamZero &zero) {
+  hipExtLaunchKernelGGL((k_stream<EPI, MT, C, NW, TRQ, ATOM>), dim3(static_cast<unsigned>(blocks)),
                         dim3(NW * 64), 0, s, t.start, t.stop, 0, static_cast<const uint16_t *>(A),
                         lda, static_cast<int>(M), static_cast<int>(ks),
                         static_cast<const u32x4_t *>(W), static_cast<int>(n_units), S, out, ldo,
-                        static_cast<int>(n_store), static_cast<int>(ks_out), scratch, counters);
+                        static_cast<int>(n_store), static_cast<int>(ks_out), scratch, counters,
+                        zero.out, zero.n);
   return hipGetLastError();
 }
 
-template <int EPI, int MT, int C>
+template <int EPI, int MT, int C, bool ATOM = false>
 hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, const void *W,
                              int64_t n_cb, int S, void *out, int64_t ldo, int64_t n_store,
                              int64_t ks_out, const StreamScratch &ws, hipStream_t s,
-                             const Timing &t = Timing()) {
+                             const Timing &t, const StreamZero &zero) {
   const int64_t groups = (M + 32 * MT - 1) / (32 * MT);
   const int64_t n_units = n_cb / C;
   const int64_t blocks = n_units * S * groups;
   if (n_cb % C || S < 1 || blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if constexpr (ATOM) {
+    // atomic halves: exactly two slices (deterministic), no scratch
+    if (S != 2) return hipErrorInvalidConfiguration;
+    return launch_stream_nw<EPI, MT, C, kStreamAtomWaves, 4, true>(
+        A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store, ks_out, nullptr, nullptr, s, t, zero);
+  }
   // Slices park MT * C blocks of 1024 sums per workgroup and count in per (group, unit):
   // refuse a launch whose scratch or counters would not fit the caller's workspace.
   if (S > 1 && (!ws.buf || !ws.cnt || groups * n_units * S * MT * C * 1024 > ws.floats ||
@@ -380,22 +415,22 @@ hipError_t launch_stream_cfg(const void *A, int64_t lda, int64_t M, int64_t ks, 
       if (stream_waves(first, S) == 4) {
         if (M <= 8)
           return launch_stream_nw<EPI, MT, C, 4, 1>(A, lda, M, ks, W, n_units, blocks, S, out,
-                                                           ldo, n_store, ks_out, scratch, counters, s, t);
+                                                           ldo, n_store, ks_out, scratch, counters, s, t, zero);
         return launch_stream_nw<EPI, MT, C, 4, 2>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
-                                                         n_store, ks_out, scratch, counters, s, t);
+                                                         n_store, ks_out, scratch, counters, s, t, zero);
       }
       if (M <= 8)
         return launch_stream_nw<EPI, MT, C, 8, 1>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
-                                                         n_store, ks_out, scratch, counters, s, t);
+                                                         n_store, ks_out, scratch, counters, s, t, zero);
       return launch_stream_nw<EPI, MT, C, 8, 2>(A, lda, M, ks, W, n_units, blocks, S, out, ldo,
-                                                       n_store, ks_out, scratch, counters, s, t);
+                                                       n_store, ks_out, scratch, counters, s, t, zero);
     }
   }
   if (stream_waves(tokens_row_major(EPI), S) == 4)
     return launch_stream_nw<EPI, MT, C, 4>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
-                                           ks_out, scratch, counters, s, t);
+                                           ks_out, scratch, counters, s, t, zero);
   return launch_stream_nw<EPI, MT, C, 8>(A, lda, M, ks, W, n_units, blocks, S, out, ldo, n_store,
-                                         ks_out, scratch, counters, s, t);
+                                         ks_out, scratch, counters, s, t, zero);
 }
 
 StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
@@ -427,38 +462,66 @@ StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks) {
   return p;
 }
 
+StreamPlan stream_plan_out(int64_t M, int64_t n_cb, int64_t ks, bool out_f32) {
+  StreamPlan p = stream_plan(M, n_cb, ks);
+  const int64_t groups = (M + 32 * p.mt - 1) / (32 * p.mt);
+  // The second product with an fp32 output and no slices of its own: two column
+  // blocks per workgroup over half the contraction each, the halves added into the
+  // zeroed output.  Each workgroup then loads the token operand for its half only,
+  // once for both blocks: the per-CU load traffic drops by a quarter (one token
+  // tile) or a third (two).
+  if (out_f32 && groups == 1 && p.s == 1 && n_cb % 2 == 0 && (ks / 2) >= 4) {
+    p.c = 2;
+    p.s = 2;
+    p.atom = 1;
+  }
+  return p;
+}
+
 template <int E>
 static hipError_t launch_epi(const StreamPlan &plan, const void *A, int64_t lda, int64_t M,
                              int64_t ks, const void *W, int64_t n_cb, void *out, int64_t ldo,
                              int64_t n_store, int64_t ks_out, const StreamScratch &ws,
-                             hipStream_t s, const Timing &t) {
+                             hipStream_t s, const Timing &t, const StreamZero &zero) {
+  if (plan.atom) {
+    // two column blocks, two atomic contraction halves (fp32 output only)
+    if constexpr (E == EPI_OUT_F32) {
+      if (plan.c != 2) return hipErrorInvalidConfiguration;
+      if (plan.mt == 1)
+        return launch_stream_cfg<E, 1, 2, true>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store,
+                                                ks_out, ws, s, t, zero);
+      return launch_stream_cfg<E, 2, 2, true>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store,
+                                              ks_out, ws, s, t, zero);
+    }
+    return hipErrorInvalidConfiguration;
+  }
   if (plan.c != 1) return hipErrorInvalidConfiguration;  // wider groups are not instantiated
   if (plan.mt == 1)
     return launch_stream_cfg<E, 1, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
-                                      ws, s, t);
+                                      ws, s, t, zero);
   return launch_stream_cfg<E, 2, 1>(A, lda, M, ks, W, n_cb, plan.s, out, ldo, n_store, ks_out,
-                                    ws, s, t);
+                                    ws, s, t, zero);
 }
 
 hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, int64_t lda,
                               int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
                               int64_t ldo, int64_t n_store, int64_t ks_out, const StreamScratch &ws,
-                              hipStream_t s, const Timing &t) {
+                              hipStream_t s, const Timing &t, const StreamZero &zero) {
   switch (epi) {
     case EPI_SILU_GATE:
-      return launch_epi<EPI_SILU_GATE>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_SILU_GATE>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_TANH:
-      return launch_epi<EPI_TANH>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_TANH>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_IDENTITY:
-      return launch_epi<EPI_IDENTITY>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_IDENTITY>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_OUT_F32:
-      return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_OUT_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_OUT_BF16:
-      return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_OUT_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_PROJ_F32:
-      return launch_epi<EPI_PROJ_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_PROJ_F32>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     case EPI_PROJ_BF16:
-      return launch_epi<EPI_PROJ_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t);
+      return launch_epi<EPI_PROJ_BF16>(plan, A, lda, M, ks, W, n_cb, out, ldo, n_store, ks_out, ws, s, t, zero);
     default:
       return hipErrorInvalidValue;
   }

@@ -118,12 +118,29 @@ struct Sizes {
 // blocks per workgroup (c) and contraction slices (s).
 struct StreamPlan {
   int mt, c, s;
+  int atom = 0;  // s == 2 contraction halves added atomically into a zeroed fp32 output
 };
+
+// A clear of `n` fp32 outputs (a multiple of 4, 16-byte aligned) done as a side job
+// by a launch, for the next launch on the stream to add into.
+struct StreamZero {
+  float *out = nullptr;
+  int64_t n = 0;
+};
+
+// Waves per workgroup of the atomic-halves second product.
+constexpr int kStreamAtomWaves = 4;
 
 // The streaming shape the library uses for M tokens against n_cb column blocks
 // and ks k-steps.  Contraction slices (s > 1) only come with one token group
 // (M <= 64).
 StreamPlan stream_plan(int64_t M, int64_t n_cb, int64_t ks);
+
+// The shape of a second product (packed hidden tokens) with M tokens: stream_plan's,
+// or, for an fp32 output that stream_plan does not slice, two column blocks per
+// workgroup over two atomic contraction halves (the output must then be zeroed
+// before the launch, e.g. by the first product's StreamZero).
+StreamPlan stream_plan_out(int64_t M, int64_t n_cb, int64_t ks, bool out_f32);
 
 // Workspace of the streaming contraction slices: sums parked by the slices
 // (`floats` of room) and the per-unit arrival counters (`n_counters` of room,
@@ -163,7 +180,7 @@ hipError_t launch_stream_gemm(int epi, const StreamPlan &plan, const void *A, in
                               int64_t M, int64_t ks, const void *W, int64_t n_cb, void *out,
                               int64_t ldo, int64_t n_store, int64_t ks_out,
                               const StreamScratch &ws, hipStream_t s,
-                              const Timing &t = Timing());
+                              const Timing &t = Timing(), const StreamZero &zero = StreamZero());
 
 // Zero n ints (a plain kernel, so it may be captured in a graph).
 hipError_t launch_zero_i32(int *p, int64_t n, hipStream_t s);
