@@ -1,23 +1,27 @@
-// Matrix-core GEMM for large token counts (prefill), one wave per SIMD.
+// Matrix-core GEMM for large token counts (prefill).
 //
 // At prefill sizes each weight element meets thousands of tokens, so both
 // projections of the shard are compute-bound (page "7.4 推理侧并行", section 7.4.1:
 // prefill is one large matrix multiply).  The kernel is shaped around what limits a
 // gfx950 compute unit when the matrix cores are meant to stay busy:
 //
-//  * Block tile 256 x 256 (tokens x columns), 4 waves, one per SIMD, each owning a
-//    128 x 128 sub-tile: 16 MFMA 32x32x16 tiles whose 256 fp32 sums per lane live in
-//    the accumulation registers (AGPRs), so the ordinary registers hold only the
-//    operand fragments and addresses.  Per k-step of 16 a wave reads 4 token and 4
-//    weight fragments (8 KiB) from LDS for 16 products: a third less LDS traffic
-//    per flop than 128 x 64 sub-tiles.  (An 8-wave 128 x 64 form is instantiated
-//    too, for comparison.)
-//  * Operands go from global memory straight into LDS (global_load_lds: no register
-//    staging) through a ring of R stages of 32 contraction indices (32 KiB each), so
-//    R - 1 stages are in flight while one is multiplied: the loads of a stage have
-//    about (R - 1) stages of products (3 to 4 k-steps of 512 cycles each) to land,
-//    which covers the latency of operands that miss L2.  A wave waits only for its
-//    own loads of the next stage, then one plain barrier per stage.
+//  * Block tile 256 x 256 (tokens x columns), 8 waves (two per SIMD), each owning a
+//    128 x 64 sub-tile: 8 MFMA 32x32x16 tiles, 128 fp32 sums per lane.  Per k-step of
+//    16 a wave reads 4 token and 2 weight fragments (6 KiB) from LDS for 8 products;
+//    the second wave on the SIMD issues its products while the first waits on its
+//    fragment reads.  The template also builds a 4-wave form (NW = 4: one wave per
+//    SIMD, 128 x 128 sub-tiles, the 256 sums per lane in the accumulation registers,
+//    a third less LDS traffic per flop); it measured 10% slower on the gate/up
+//    product and level on the down product, since a lone wave has nothing to issue
+//    while it waits, so the library launches the 8-wave form.
+//  * Operands go from global memory straight into LDS through a ring of R stages of
+//    32 contraction indices (32 KiB each: 16 token and 16 weight chunks of 1 KiB), so
+//    R - 1 stages are in flight while one is multiplied.  The library form (GF_BUF)
+//    uses buffer loads to LDS: one 32-bit lane offset per chunk and the stage advance
+//    in a scalar offset, where 64-bit global addresses cost two vector additions per
+//    chunk per stage.  A wave waits only for its own loads of the next stage (an
+//    exact count of its outstanding loads), then one plain barrier per stage; the
+//    loop is peeled so that the steady-state stages carry no branch around a load.
 //  * The weight and the packed hidden buffer arrive in fragment order
 //    (tpm_internal.h): one conflict-free 1 KiB ds_read_b128 per fragment.  Row-major
 //    tokens are loaded as 64-byte row segments, four lanes per row, into a swizzled
