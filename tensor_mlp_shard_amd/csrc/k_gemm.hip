@@ -437,7 +437,10 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     // The stores above are complete at the coherence point once the wave's memory
-    // counters drain (s_waitcnt 0); only then is the workgroup counted in.
+    // counters drain (s_waitcnt 0); only then is the workgroup counted in.  As in the
+    // streaming kernel's slice hand-off, the ordering rests on the emitted code (sc1
+    // stores and loads, the wait and the barrier before the counter), which
+    // tests/test_handoff_asm.py checks, not on relaxed atomics' language semantics.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {

@@ -316,6 +316,14 @@ k_stream(const uint16_t *__restrict__ A, int64_t lda, int M, int ks,
   // then one thread counts the workgroup in.  The scratch traffic never touches a
   // non-coherent cache line, so no cache write-back or invalidation is needed
   // (those would also evict the weight stream of the other workgroups on the XCD).
+  // The ordering rests on the code emitted for gfx950, not on the language memory
+  // model (a relaxed counter orders nothing there): the parked sums are agent-scope
+  // atomic stores (the sc1 bit: written through to the device coherence point), the
+  // explicit wait below holds every wave until they are acknowledged there, the barrier
+  // holds thread 0 until every wave has waited, and the last arriver reads the sums
+  // with agent-scope atomic loads (sc1: at the coherence point, never from a stale line
+  // of its own L2).  tests/test_handoff_asm.py checks these properties in the compiled
+  // kernels.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {

@@ -329,7 +329,10 @@ k_tiled(const uint16_t *__restrict__ A, int64_t lda, int M, int k_total,
   if (split) {
     // Park this half's sums (write-through stores: complete at the device
     // coherence point once counted), count the workgroup in; the second to
-    // arrive reads the other half's sums with coherent loads and goes on.
+    // arrive reads the other half's sums with coherent loads and goes on.  The
+    // ordering rests on the emitted code (sc1 stores and loads, the wait and the
+    // barrier before the counter), which tests/test_handoff_asm.py checks, not on
+    // relaxed atomics' language semantics.
     __shared__ int s_second;
     constexpr int NV = 4 * WNB * 8;  // 64-bit pairs of sums per thread
     uint64_t *mine = split_buf + (static_cast<int64_t>(pair) * 2 + khalf) * (NW * 64 * NV);
