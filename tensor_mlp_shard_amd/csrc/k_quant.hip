@@ -10,7 +10,8 @@
 //  * k_quant_fp8: one workgroup per token row; the row's largest magnitude sets
 //    the row scale s = amax / 448 (448 = largest finite E4M3 value), each element
 //    is stored as the E4M3 code of x * (448 / amax), rounded to nearest, ties to
-//    even, saturating at +-448.  A zero row gets scale 1 and all-zero codes.
+//    even, saturating at +-448 (the hardware FP8 conversion).  A zero row gets scale
+//    1 and all-zero codes.
 //  * k_reduce_fp8: element-wise, z = sum_i value(code_i) * s_i in rank order in
 //    fp32; the codes are decoded by the hardware FP8 conversion, which reads OCP
 //    E4M3 on gfx950.
@@ -25,24 +26,24 @@
 
 namespace tpm {
 
-// E4M3 code of x: round to nearest even on the E4M3 grid, saturate to +-448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (!(a == a)) return sign | 0x7fu;  // NaN
-  if (a >= 448.0f) return sign | 0x7eu;
-  // spacing of the grid around a: 2^(E - 3) for a >= 2^-6, 2^-9 below
-  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xff) - 127;
-  const int el = e < -6 ? -6 : e;
-  const float q = rintf(ldexpf(a, 3 - el));  // multiples of the spacing, ties to even
-  const float v = ldexpf(q, el - 3);          // the rounded magnitude (exact)
-  if (v >= 448.0f) return sign | 0x7eu;
-  if (v < 0.015625f) return sign | static_cast<uint32_t>(q);  // subnormal (q < 8), or 0
-  // normal: v = (8 + m) 2^(E' - 3) with 8 <= 8 + m < 16 (rounding may carry into the
-  // next binade, where q = 16 and the exponent is one higher)
-  const int ev = static_cast<int>((__float_as_uint(v) >> 23) & 0xff) - 127;
-  const uint32_t m = static_cast<uint32_t>(ldexpf(v, 3 - ev)) - 8u;
-  return sign | (static_cast<uint32_t>(ev + 7) << 3) | m;
+// E4M3 codes of four fp32 values, packed little-endian into a word: the hardware
+// conversion (v_cvt_pk_fp8_f32, OCP E4M3, round to nearest even).  On every finite
+// value below 464 in magnitude it gives the code the definition asks for (checked on
+// MI355X against a software rounding on the E4M3 grid for all 2^32 fp32 inputs: no
+// difference below 464), and a finite row never produces more than 448 (1 + 2^-22).
+// Clamping to +-448 first keeps the saturation of infinite products (a row whose amax
+// is so small that 448 / amax overflows); NaN products take the NaN code 0x7f.
+__device__ __forceinline__ uint32_t e4m3_x4(const float (&y)[4]) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(y[i], -448.0f), 448.0f);
+  int t = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  t = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], t, true);
+  uint32_t b = static_cast<uint32_t>(t);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (!(y[i] == y[i])) b = (b & ~(0xffu << (8 * i))) | (0x7fu << (8 * i));
+  return b;
 }
 
 template <int IN>
@@ -109,10 +110,10 @@ k_quant_fp8(const void *__restrict__ x, int cols16, u32x4_t *__restrict__ q,
       u32x4_t o;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        uint32_t b = 0;
+        float y[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b |= f32_to_e4m3(__fmul_rn(v[j][4 * w + i], inv)) << (8 * i);
-        o[w] = b;
+        for (int i = 0; i < 4; ++i) y[i] = __fmul_rn(v[j][4 * w + i], inv);
+        o[w] = e4m3_x4(y);
       }
       q[row0 + c] = o;
     }

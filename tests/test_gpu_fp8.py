@@ -47,6 +47,32 @@ def test_quantize_bit_exact(rows, cols, dt):
     assert torch.equal(q, torch.from_numpy(rq))
 
 
+def test_quantize_every_rounding_case():
+    """Each E4M3 decision the quantizer can face, through the library: rows that start
+    with 448 have amax 448, so the scale is 1 and every other entry is encoded as given.
+    The entries are every E4M3 grid value, every midpoint between neighbours (the ties,
+    subnormal ones included) and the fp32 values just below and above each midpoint,
+    for both signs; codes must equal the oracle's table search bit for bit."""
+    import numpy as np
+    grid = np.array(sorted({abs(float(oracle.e4m3_value(c))) for c in range(256)
+                            if np.isfinite(oracle.e4m3_value(c))}), dtype=np.float32)
+    mids = ((grid[:-1].astype(np.float64) + grid[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (grid[:-1].astype(np.float64) + grid[1:]) / 2)
+    vals = np.concatenate([grid, mids, np.nextafter(mids, np.float32(0)),
+                           np.nextafter(mids, np.float32(np.inf))]).astype(np.float32)
+    cols = 16 * ((len(vals) + 1 + 15) // 16)
+    x = np.zeros((2, cols), dtype=np.float32)
+    x[:, 0] = 448.0
+    x[0, 1:1 + len(vals)] = vals
+    x[1, 1:1 + len(vals)] = -vals
+    say("fp8 rounding cases:", len(vals), "magnitudes, both signs")
+    q, s = quant_gpu(torch.from_numpy(x))
+    rq, rs = oracle.quantize_fp8(x)
+    assert np.all(rs == 1.0) and torch.equal(s, torch.from_numpy(rs))
+    bad = np.nonzero(q.numpy() != rq)
+    assert bad[0].size == 0, [(float(x[r, c]), int(q[r, c]), int(rq[r, c])) for r, c in zip(*bad)][:10]
+
+
 @pytest.mark.parametrize("k", [1, 2, 8, 16])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_reduce_fp8(k, out_dtype):
