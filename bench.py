@@ -215,6 +215,16 @@ def run_decode_graph(lib, ranks, red_args, steps, warmup):
     return t1 - t0, g
 
 
+def run_fwd_graph(lib, ranks, reps):
+    """Time per tp_mlp_shard_fwd call as the stream sees it (both launches and the gap
+    between them): one pass over the ranks captured in a HIP graph, replayed `reps`
+    times; replay time / number of ranks."""
+    g = _graph_of(lambda sp: [r.fwd(sp) for r in ranks])
+    t = _time_graph(g, reps) / len(ranks)
+    del g
+    return t
+
+
 def _sleep_cycles_per_ms():
     """Rate of torch's bounded spin kernel (cycles per ms), measured on the device."""
     import torch
@@ -835,6 +845,7 @@ def main():
     log("decode: the same %d steps launched eagerly, each kernel timed by its own events ..."
         % args.steps)
     elapsed_eager, k1, k2 = run_decode_eager(lib, ranks, red_args, args.steps, args.warmup)
+    fwd_s = run_fwd_graph(lib, ranks, args.steps)
     ms_step_eager = elapsed_eager / args.steps * 1e3
 
     F = FFN // TP
@@ -860,6 +871,7 @@ def main():
             "min_launch_us": round(min(k2) * 1e3, 2),
             "achieved_GBs": round(k2_bytes / (k2_ms * 1e-3) / 1e9, 1)}
     shard_us = (k1_ms + k2_ms) * 1e3
+    fwd_us = fwd_s * 1e6
     shard_bytes = w_bytes_rank + M_DECODE * D_MODEL * 2 + M_DECODE * D_MODEL * 4
     log("decode: %.3f ms/step (graph), %.3f ms/step (eager), %.1f GB/s weights; "
         "gate/up %.2f us, down %.2f us" % (ms_step, ms_step_eager, value, k1_ms * 1e3, k2_ms * 1e3))
@@ -946,7 +958,13 @@ def main():
         "down_projection": down,
         "decode_shard": {"avg_us": round(shard_us, 2),
                          "GBs": round(shard_bytes / (shard_us * 1e-6) / 1e9, 1),
-                         "algorithmic_bytes": shard_bytes},
+                         "algorithmic_bytes": shard_bytes,
+                         "fwd_us": round(fwd_us, 2),
+                         "fwd_frac_of_hbm_peak": round(shard_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "avg_us: the two kernels' own durations (launch-attached "
+                                 "events); fwd_us: the whole tp_mlp_shard_fwd as the stream "
+                                 "sees it, gap between the launches included: one pass over "
+                                 "the 8 ranks captured in a HIP graph, replay time / 8"},
         "prefill": prefill,
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,

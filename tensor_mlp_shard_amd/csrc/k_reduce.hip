@@ -110,10 +110,13 @@ hipError_t launch_reduce(const void *const *parts, int k, int64_t numel, int in_
   PartPtrs pp = {};
   for (int i = 0; i < k; ++i) pp.p[i] = parts[i];
   const int64_t n8 = numel >> 3;
-  int64_t blocks = (n8 + 255) / 256;
+  // small blocks so that a decode-size sum (32 K chunks of 8) still spreads over every
+  // compute unit: 512 workgroups of 64 threads rather than 128 of 256
+  const int bs = n8 >= (int64_t(1) << 18) ? 256 : 64;
+  int64_t blocks = (n8 + bs - 1) / bs;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
-  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  dim3 grid(static_cast<unsigned>(blocks)), block(bs);
   if (in_dtype == TPM_F32 && out_dtype == TPM_F32)
     hipLaunchKernelGGL((k_reduce<TPM_F32, TPM_F32>), grid, block, 0, s, pp, k, numel, out);
   else if (in_dtype == TPM_F32)
