@@ -43,6 +43,15 @@ __device__ __forceinline__ f32x16_t mfma_32x32x16(const u32x4_t a, const u32x4_t
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// D = A(16x32) * B(32x16) + C on the matrix cores.  Lane l supplies
+// A[l % 16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l % 16]; it receives
+// D[4*(l/16) + r][l % 16] in register r (0..3).  (Checked on MI355X with small
+// integer operands.)
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const u32x4_t a, const u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Contraction index of element i (0..7) of lane half h in k-step s (fragment order).
 __host__ __device__ __forceinline__ int kappa(int s, int h, int i) {
   return 32 * (s >> 1) + 16 * h + 8 * (s & 1) + i;

@@ -6,19 +6,23 @@
 // gfx950 compute unit when the matrix cores are meant to stay busy:
 //
 //  * Block tile 256 x 256 (tokens x columns), 8 waves (two per SIMD), each owning a
-//    128 x 64 sub-tile: 8 MFMA 32x32x16 tiles, 128 fp32 sums per lane.  Per k-step of
-//    16 a wave reads 4 token and 2 weight fragments (6 KiB) from LDS for 8 products;
-//    the second wave on the SIMD issues its products while the first waits on its
-//    fragment reads.  The template also builds a 4-wave form (NW = 4: one wave per
-//    SIMD, 128 x 128 sub-tiles, the 256 sums per lane in the accumulation registers,
-//    a third less LDS traffic per flop); it measured 10% slower on the gate/up
-//    product and level on the down product, since a lone wave has nothing to issue
-//    while it waits, so the library launches the 8-wave form.
+//    128 x 64 sub-tile: 128 fp32 sums per lane.  The library multiplies with 16x16x32
+//    products (GF_M16: 32 per stage per wave, 8 row blocks x 4 column blocks), which
+//    move fewer register bytes per flop than 32x32x16 ones: flat out on every SIMD the
+//    16x16x32 loop holds a 2.14 GHz shader clock against 1.77 GHz for 32x32x16, and
+//    since the prefill products are power-limited that clock is what they gain (gate/up
+//    of the TP=8 shard at M = 8192: 785-792 -> 701-716 us).  Their fragments are
+//    gathered from the same 32x32x16 operand order with a per-lane remap (see
+//    fragA16 / fragB16).  Per stage a wave reads 8 token and 4 weight fragments (12
+//    KiB) from LDS; the second wave on the SIMD issues its products while the first
+//    waits on its reads.  The template also builds the 32x32x16 form and a 4-wave
+//    form (NW = 4: one wave per SIMD, 128 x 128 sub-tiles, a third less LDS traffic
+//    per flop), both slower here (the lone wave has nothing to issue while it waits).
 //  * Operands go from global memory straight into LDS through a ring of R stages of
 //    32 contraction indices (32 KiB each: 16 token and 16 weight chunks of 1 KiB), so
-//    R - 1 stages are in flight while one is multiplied.  The library form (GF_BUF)
-//    uses buffer loads to LDS: one 32-bit lane offset per chunk and the stage advance
-//    in a scalar offset, where 64-bit global addresses cost two vector additions per
+//    R - 1 stages are in flight while one is multiplied (R = 3 in the library).  The
+//    library form (GF_BUF) uses buffer loads to LDS: one 32-bit lane offset per chunk
+//    and the stage advance in a scalar offset, where 64-bit global addresses cost two vector additions per
 //    chunk per stage.  A wave waits only for its own loads of the next stage (an
 //    exact count of its outstanding loads), then one plain barrier per stage; the
 //    loop is peeled so that the steady-state stages carry no branch around a load.
@@ -36,9 +40,11 @@
 //    of two values is order-free, so the result does not depend on arrival order)
 //    and runs the epilogue.
 //  * Fused epilogue: SiLU(gate) * up (a 32-column block holds 16 gate and the 16
-//    matching up columns; lane c meets lane c + 16 by a cross-lane exchange), tanh or
-//    identity, staged through LDS and written as bf16 in the packed hidden order; or
-//    the row-major partial store (fp32 or bf16).
+//    matching up columns: with 16x16x32 products they are two accumulator blocks and
+//    a feature's gate and up sums sit in the same lane; with 32x32x16 lane c meets
+//    lane c + 16 by a cross-lane exchange), tanh or identity, staged through LDS and
+//    written as bf16 in the packed hidden order; or the row-major partial store (fp32
+//    or bf16).
 #include <type_traits>
 
 #include "device_common.h"
@@ -91,15 +97,30 @@ struct GemmShape {
   static constexpr int NF = 4 + WNB;              // fragments per k-step per wave
 };
 
+// Accumulators of a wave's 128 x (32 WNB) sub-tile, 128 fp32 per lane either way:
+// 32x32x16 products hold acc[i][j] for 32-row block i and 32-column block j (16 sums
+// per lane); 16x16x32 products hold acc[i][j] for 16-row block i and 16-column block j
+// (4 sums per lane).
+template <int NW, bool M16>
+struct GemmAcc {
+  static constexpr int WNB = 16 / NW;
+  static constexpr int AI = M16 ? 8 : 4;         // row blocks
+  static constexpr int AJ = M16 ? 2 * WNB : WNB;  // column blocks
+  static constexpr int RPA = M16 ? 4 : 16;       // sums per lane per block
+  using T = std::conditional_t<M16, f32x4_t, f32x16_t>;
+};
+
 // Epilogue of a 256 x 256 tile held by NW waves as 128 x (32 WNB) sub-tiles (wave at
 // row half wm, column group wn): SiLU(gate) * up, tanh or identity written as bf16 into
 // the packed hidden buffer (staged through the LDS ring, free after the main loop), or
 // the row-major partial store.
-template <int EPI, int NW, int R>
-__device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[4][16 / NW], u32x4_t (*lds)[kStageChunks][64],
+template <int EPI, int NW, int R, bool M16, typename AccT, int AI, int AJ>
+__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[AI][AJ], u32x4_t (*lds)[kStageChunks][64],
                                               int wave, int wm, int wn, int lane, int tn, int row0,
                                               int M, void *__restrict__ out, int64_t ldo, int n_store,
                                               int ks_out) {
+  using Ac = GemmAcc<NW, M16>;
+  static_assert(AI == Ac::AI && AJ == Ac::AJ, "accumulator layout");
   constexpr int WNB = 16 / NW;
   constexpr bool HIDDEN = writes_hidden(EPI);
   if constexpr (HIDDEN) {
@@ -118,18 +139,38 @@ __device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[4][16 / NW], u32x4
 #pragma unroll
       for (int jj = 0; jj < BPP; ++jj) {
         const int j = pass * BPP + jj;
+        if constexpr (M16) {
+          // 32-column block j is 16-column blocks 2 j (gate, or its first half) and
+          // 2 j + 1 (up, or its second half): gate and up of a feature share a lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < Ac::AI; ++i) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = i * 32 + mfma32_row(r, lane);
-            const int c = lane & 31;
-            const float v = acc[i][j][r];
-            if constexpr (EPI == EPI_SILU_GATE) {
-              const float u = __shfl_xor(v, 16);
-              if (c < 16) hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
-            } else {
-              hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
+            for (int r = 0; r < 4; ++r) {
+              const int rr = 16 * i + 4 * (lane >> 4) + r;
+              const int c = lane & 15;
+              const float v = acc[i][2 * j][r], u = acc[i][2 * j + 1][r];
+              if constexpr (EPI == EPI_SILU_GATE) {
+                hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
+              } else {
+                hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
+                hs[rr * HS + jj * 32 + 16 + c] = f32_to_bf16(act_f<EPI>(u));
+              }
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < Ac::AI; ++i) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rr = i * 32 + mfma32_row(r, lane);
+              const int c = lane & 31;
+              const float v = acc[i][j][r];
+              if constexpr (EPI == EPI_SILU_GATE) {
+                const float u = __shfl_xor(v, 16);
+                if (c < 16) hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
+              } else {
+                hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
+              }
             }
           }
         }
@@ -150,14 +191,16 @@ __device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[4][16 / NW], u32x4
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < Ac::AI; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + (wm * 4 + i) * 32 + mfma32_row(r, lane);
+      for (int r = 0; r < Ac::RPA; ++r) {
+        const int row = row0 + wm * 128 +
+                        (M16 ? 16 * i + 4 * (lane >> 4) + r : 32 * i + mfma32_row(r, lane));
         if (row >= M) continue;
 #pragma unroll
-        for (int j = 0; j < WNB; ++j) {
-          const int col = (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
+        for (int j = 0; j < Ac::AJ; ++j) {
+          const int col = M16 ? (tn * 8 + wn * WNB) * 32 + 16 * j + (lane & 15)
+                              : (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
           const int64_t o = static_cast<int64_t>(row) * ldo + col;
           if constexpr (stores_f32(EPI)) {
             if (col < n_store) static_cast<float *>(out)[o] = acc[i][j][r];
@@ -172,9 +215,11 @@ __device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[4][16 / NW], u32x4
 
 // Kernel flags: GF_BUF loads the operands with buffer instructions (one 32-bit lane
 // offset per chunk, the stage advance in a scalar offset) instead of 64-bit global
-// addresses; GF_AGPR keeps the accumulators in the accumulation registers.
+// addresses; GF_AGPR keeps the accumulators in the accumulation registers; GF_M16
+// multiplies with 16x16x32 products instead of 32x32x16.
 constexpr int GF_BUF = 1;
 constexpr int GF_AGPR = 2;
+constexpr int GF_M16 = 4;
 
 // Buffer descriptor of a raw byte-addressed buffer (gfx9 layout: dword 3 = 0x00020000,
 // 32-bit data format, no swizzle); every access made through it stays in bounds by
@@ -198,6 +243,7 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
        int64_t ldo, int n_store, int ks_out, int n_whole, uint64_t *__restrict__ split_buf,
        int *__restrict__ split_cnt) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
+  constexpr bool M16 = (FL & GF_M16) != 0;       // 16x16x32 products
   using Sh = GemmShape<NW>;
   constexpr int WNB = Sh::WNB, NF = Sh::NF;
   constexpr int PT = 16 / NW;   // token chunks each wave loads per stage
@@ -296,15 +342,17 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     }
   };
 
-  f32x16_t acc[4][WNB];
+  using Ac = GemmAcc<NW, M16>;
+  typename Ac::T acc[Ac::AI][Ac::AJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < Ac::AI; ++i)
 #pragma unroll
-    for (int j = 0; j < WNB; ++j)
+    for (int j = 0; j < Ac::AJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < Ac::RPA; ++r) acc[i][j][r] = 0.0f;
   auto mma = [&](int i, int j, const u32x4_t &a, const u32x4_t &w) {
-    acc[i][j] = mfma_32x32x16(a, w, acc[i][j]);
+    if constexpr (M16) acc[i][j] = mfma_16x16x32(a, w, acc[i][j]);
+    else acc[i][j] = mfma_32x32x16(a, w, acc[i][j]);
     if constexpr ((FL & GF_AGPR) != 0) asm("" : "+a"(acc[i][j]));
   };
 
@@ -326,6 +374,24 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     }
     return lds[buf][16 + 8 * ks + WNB * wn + (f - 4)][lane];
   };
+  // 16x16x32 fragments of a whole stage (its 32 contraction indices), gathered from
+  // the same chunks: the k-group g = lane / 16 of a 16x16x32 operand is k-step g & 1,
+  // lane half g >> 1 of the stage's 32x32x16 pair, so A and B agree on the order.
+  // Each 16-lane group reads 256 contiguous bytes (or, for row-major tokens, the same
+  // swizzled slots a 32x32x16 read uses), free of bank conflicts.
+  const int g16 = lane >> 4, r16 = lane & 15;
+  auto fragA16 = [&](int buf, int ri) -> u32x4_t {  // rows 16 ri .. 16 ri + 15 of the wave's 128
+    const int row = wm * 128 + 16 * ri + r16;        // row of the tile
+    if constexpr (FIRST) {
+      return lds_flat[(buf * kStageChunks + (row >> 4)) * 64 + tok_slot + (g16 ^ tok_x)];
+    } else {
+      return lds[buf][8 * (g16 & 1) + (row >> 5)][32 * (g16 >> 1) + (row & 31)];
+    }
+  };
+  auto fragB16 = [&](int buf, int cj) -> u32x4_t {  // columns 16 cj .. of the wave's 32 WNB
+    const int cb = WNB * wn + (cj >> 1);
+    return lds[buf][16 + 8 * (g16 & 1) + cb][32 * (g16 >> 1) + 16 * (cj & 1) + r16];
+  };
 
   // Wait until this wave's loads of stage kt + 1 have landed (later stages may stay
   // in flight) and its LDS reads are done, then meet the other waves: after the
@@ -338,8 +404,19 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  auto sync_mid = [&](int kt, auto refill_c) {
+    if constexpr (decltype(refill_c)::value) {
+      wait_vmem<(R - 2) * PW>();  // stages kt + 2 .. kt + R - 1 stay in flight
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      sync_next(kt);
+    }
+  };
 
-  // Prologue: R stages in flight, then stage 0's first k-step in registers.
+  // Prologue: R stages in flight, then stage 0's first fragments in registers.
 #pragma unroll
   for (int st = 0; st < R; ++st)
     if (st < k_n) {
@@ -351,9 +428,19 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  u32x4_t f0[NF], f1[NF];
+  // 32x32x16: NF fragments of a k-step; 16x16x32: 4 A and 2 WNB B fragments
+  constexpr int NFR = M16 ? 4 + 2 * WNB : NF;
+  u32x4_t f0[NFR], f1[NFR];
+  if constexpr (M16) {
+    // f0[0..3]: A row blocks 0..3, f0[4..4 + AJ): the B blocks; f1[0..3]: A 4..7
 #pragma unroll
-  for (int f = 0; f < NF; ++f) f0[f] = frag(0, 0, f);
+    for (int i = 0; i < 4; ++i) f0[i] = fragA16(0, i);
+#pragma unroll
+    for (int j = 0; j < Ac::AJ; ++j) f0[4 + j] = fragB16(0, j);
+  } else {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) f0[f] = frag(0, 0, f);
+  }
 
   // Stage kt: k-step 0 multiplies f0 while k-step 1's fragments are read into f1;
   // then (sync) k-step 1 multiplies f1 while the buffer of stage kt is refilled
@@ -361,7 +448,7 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   // scheduling barriers keep one fragment read or load between products.  REFILL
   // and MORE are compile-time so the steady-state loop has no branches: the last R
   // stages run in a peeled tail.
-  auto stage = [&](int kt, int buf, auto refill_c, auto more_c) {
+  auto stage32 = [&](int kt, int buf, auto refill_c, auto more_c) {
     constexpr bool REFILL = decltype(refill_c)::value;
     constexpr bool MORE = decltype(more_c)::value;
     const int nbuf = buf + 1 == R ? 0 : buf + 1;
@@ -376,17 +463,7 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if constexpr (MORE) {
-      if constexpr (REFILL) {
-        wait_vmem<(R - 2) * PW>();  // stages kt + 2 .. kt + R - 1 stay in flight
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-      } else {
-        sync_next(kt);
-      }
-    }
+    if constexpr (MORE) sync_mid(kt, refill_c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -402,6 +479,49 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  // The same stage with 16x16x32 products: the first half multiplies row blocks 0..3
+  // (f0) by every column block while row blocks 4..7 are read into f1; then (sync) the
+  // second half multiplies row blocks 4..7, column block by column block, so that each
+  // B fragment is dead after its four products and the next stage's copy can be read
+  // in its place; the next stage's row blocks 0..3 are read meanwhile.
+  auto stage16 = [&](int kt, int buf, auto refill_c, auto more_c) {
+    constexpr bool REFILL = decltype(refill_c)::value;
+    constexpr bool MORE = decltype(more_c)::value;
+    constexpr int AJ = Ac::AJ;
+    const int nbuf = buf + 1 == R ? 0 : buf + 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < AJ; ++j) {
+        mma(i, j, f0[i], f0[4 + j]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j == 0) f1[i] = fragA16(buf, 4 + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (MORE) sync_mid(kt, refill_c);
+#pragma unroll
+    for (int j = 0; j < AJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mma(4 + i, j, f1[i], f0[4 + j]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int q = j * 4 + i;
+        if constexpr (REFILL)
+          if (q < PW) issue(kt + R, buf, q);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MORE) {
+          if (j == 0) f0[i] = fragA16(nbuf, i);
+          if (i == 3) f0[4 + j] = fragB16(nbuf, j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  auto stage = [&](int kt, int buf, auto refill_c, auto more_c) {
+    if constexpr (M16) stage16(kt, buf, refill_c, more_c);
+    else stage32(kt, buf, refill_c, more_c);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -422,18 +542,18 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     // point once counted), count the workgroup in; the second to arrive reads the
     // other half's sums with coherent loads and goes on.
     int *s_second = reinterpret_cast<int *>(&lds[0][0][0]);  // the ring is free now
-    constexpr int NV = 4 * WNB * 8;  // 64-bit pairs of sums per thread
+    constexpr int NV = Ac::AI * Ac::AJ * Ac::RPA / 2;  // 64-bit pairs of sums per thread
     uint64_t *mine = split_buf + (static_cast<int64_t>(pair) * 2 + khalf) * (NW * 64 * NV);
     uint64_t *other = split_buf + (static_cast<int64_t>(pair) * 2 + (khalf ^ 1)) * (NW * 64 * NV);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < Ac::AI; ++i)
 #pragma unroll
-      for (int j = 0; j < WNB; ++j)
+      for (int j = 0; j < Ac::AJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
+        for (int r = 0; r < Ac::RPA; r += 2) {
           const uint64_t v = static_cast<uint64_t>(__float_as_uint(acc[i][j][r])) |
                              (static_cast<uint64_t>(__float_as_uint(acc[i][j][r + 1])) << 32);
-          __hip_atomic_store(&mine[((i * WNB + j) * 8 + r / 2) * (NW * 64) + tid], v,
+          __hip_atomic_store(&mine[((i * Ac::AJ + j) * (Ac::RPA / 2) + r / 2) * (NW * 64) + tid], v,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     // The stores above are complete at the coherence point once the wave's memory
@@ -455,28 +575,31 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     __syncthreads();  // every wave has read the flag before the epilogue reuses the ring
     if (!second) return;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < Ac::AI; ++i)
 #pragma unroll
-      for (int j = 0; j < WNB; ++j)
+      for (int j = 0; j < Ac::AJ; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const uint64_t v = __hip_atomic_load(&other[((i * WNB + j) * 8 + r / 2) * (NW * 64) + tid],
+        for (int r = 0; r < Ac::RPA; r += 2) {
+          const uint64_t v = __hip_atomic_load(&other[((i * Ac::AJ + j) * (Ac::RPA / 2) + r / 2) * (NW * 64) + tid],
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           acc[i][j][r] += __uint_as_float(static_cast<uint32_t>(v));
           acc[i][j][r + 1] += __uint_as_float(static_cast<uint32_t>(v >> 32));
         }
   }
-  gemm_epilogue<EPI, NW, R>(acc, lds, wave, wm, wn, lane, tn, row0, M, out, ldo, n_store, ks_out);
+  gemm_epilogue<EPI, NW, R, M16>(acc, lds, wave, wm, wn, lane, tn, row0, M, out, ldo, n_store, ks_out);
 }
 
 }  // namespace tpm
 
 namespace tpm {
 
-// The configuration the library launches.
+// The configuration the library launches: 8 waves, 16x16x32 products, a 3-stage ring,
+// buffer loads (TP=8 shard at M = 8192, medians of 20 launches; gate/up / down:
+// 32x32x16 with a 4-stage ring 785-792 / 373-374 us, 16x16x32 with 4 stages 710-716 /
+// 370 us, with 3 stages 701-704 / 367-369 us; 16x16x32 on 4 waves 752-767 / 372-382 us).
 constexpr int kGemmWaves = 8;
-constexpr int kGemmRing = 4;
-constexpr int kGemmFlags = GF_BUF;
+constexpr int kGemmRing = 3;
+constexpr int kGemmFlags = GF_BUF | GF_M16;
 
 template <int EPI, int NW = kGemmWaves, int R = kGemmRing, int FL = kGemmFlags>
 hipError_t launch_gemm_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
