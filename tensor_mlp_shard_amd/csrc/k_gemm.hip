@@ -28,10 +28,15 @@
 //    loop is peeled so that the steady-state stages carry no branch around a load.
 //  * The weight and the packed hidden buffer arrive in fragment order
 //    (tpm_internal.h): one conflict-free 1 KiB ds_read_b128 per fragment.  Row-major
-//    tokens are loaded as 64-byte row segments, four lanes per row, into a swizzled
-//    layout (piece p of tile row r at slot 4 (r mod 16) + (p xor sw(r)),
-//    sw(r) = ((r >> 2) + 2 ((r >> 1) & 1)) mod 4) from which a fragment read is free
-//    of bank conflicts for any 8 or 16 consecutive lanes.
+//    tokens are loaded as 64-byte row segments of 16 rows per 1 KiB chunk.  For
+//    16x16x32 products the chunk is stored transposed (piece p of row r at slot
+//    16 p + r), so that a fragment read (lane l: row l % 16, piece l / 16) is
+//    lane-contiguous: measured on MI355X, every arrangement that keeps a row's four
+//    pieces side by side costs 4 bank-conflict cycles per such read (58.5 M per
+//    gate/up launch), the transposed one none.  For 32x32x16 products the pieces stay
+//    side by side, swizzled (slot 4 (r mod 16) + (p xor sw(r)),
+//    sw(r) = ((r >> 2) + 2 ((r >> 1) & 1)) mod 4), which that read pattern takes
+//    without conflicts.
 //  * Tiles are renumbered XCD-contiguous (workgroup b runs on XCD b mod 8) and grouped
 //    four tile rows at a time, so the tiles an XCD runs together share operands in
 //    its L2.  When the last round of tiles would leave at least half of the compute
@@ -244,6 +249,7 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
        int *__restrict__ split_cnt) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
   constexpr bool M16 = (FL & GF_M16) != 0;       // 16x16x32 products
+  constexpr bool TT = M16;                       // transposed row-major token chunks
   using Sh = GemmShape<NW>;
   constexpr int WNB = Sh::WNB, NF = Sh::NF;
   constexpr int PT = 16 / NW;   // token chunks each wave loads per stage
@@ -308,7 +314,13 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
     const int c = PT * wave + q;
-    if constexpr (FIRST) {
+    if constexpr (FIRST && TT) {
+      // transposed token chunk (16x16x32 form): lane l holds piece l / 16 of row
+      // l % 16, so that a fragment read is lane-contiguous
+      const int r = 16 * c + (lane & 15);
+      const int rr = row0 + r < M ? r : M - 1 - row0;  // rows past the end repeat the last
+      tvo[q] = static_cast<unsigned>((static_cast<int64_t>(rr) * lda + 8 * (lane >> 4)) * 2);
+    } else if constexpr (FIRST) {
       const int r = 16 * c + (lane >> 2);
       const int rr = row0 + r < M ? r : M - 1 - row0;  // rows past the end repeat the last
       const int piece = (lane & 3) ^ tok_sw(r & 15);
@@ -377,12 +389,14 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   // 16x16x32 fragments of a whole stage (its 32 contraction indices), gathered from
   // the same chunks: the k-group g = lane / 16 of a 16x16x32 operand is k-step g & 1,
   // lane half g >> 1 of the stage's 32x32x16 pair, so A and B agree on the order.
-  // Each 16-lane group reads 256 contiguous bytes (or, for row-major tokens, the same
-  // swizzled slots a 32x32x16 read uses), free of bank conflicts.
+  // Each 16-lane group reads 256 contiguous bytes (row-major tokens: the whole
+  // transposed chunk, lane by lane), free of bank conflicts.
   const int g16 = lane >> 4, r16 = lane & 15;
   auto fragA16 = [&](int buf, int ri) -> u32x4_t {  // rows 16 ri .. 16 ri + 15 of the wave's 128
     const int row = wm * 128 + 16 * ri + r16;        // row of the tile
-    if constexpr (FIRST) {
+    if constexpr (FIRST && TT) {
+      return lds_flat[(buf * kStageChunks + (row >> 4)) * 64 + lane];
+    } else if constexpr (FIRST) {
       return lds_flat[(buf * kStageChunks + (row >> 4)) * 64 + tok_slot + (g16 ^ tok_x)];
     } else {
       return lds[buf][8 * (g16 & 1) + (row >> 5)][32 * (g16 >> 1) + (row & 31)];
