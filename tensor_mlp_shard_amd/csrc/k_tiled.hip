@@ -1,8 +1,11 @@
-// LDS-tiled bf16 matrix-core GEMM for large token counts (prefill).
+// LDS-tiled bf16 matrix-core GEMM for large token counts, with a grouped mode.
 //
 // At prefill sizes each weight element meets thousands of tokens, so the
 // projections are compute-bound (page "7.4 推理侧并行", section 7.4.1: prefill is a
-// large matrix multiply).  This kernel keeps the matrix cores fed from LDS:
+// large matrix multiply).  The plain prefill products run on k_gemm.hip; this kernel
+// serves the grouped experts with many tokens per expert (one launch over every
+// expert's rows, the counts read on the device) and operands beyond the 32-bit
+// buffer offsets k_gemm.hip uses.  It keeps the matrix cores fed from LDS:
 //
 //  * Block tile 256 x 256 (tokens x columns).  NW waves: four (one per SIMD, each
 //    owning a 128 x 128 sub-tile = 4 x 4 MFMA 32x32x16 tiles, 256 fp32
