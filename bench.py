@@ -20,6 +20,8 @@ The JSON line also carries
   timing hook) over the same steps launched eagerly, against the 8 TB/s HBM peak;
 * ``prefill``: one rank shard at the prefill shape (M = 8192), TFLOP/s against the
   2.5 PFLOP/s dense bf16 matrix-core peak, with its own per-kernel event timing;
+* ``vendor_gemm``: the same two products on torch.matmul (hipBLASLt, plain bf16
+  output, no epilogue) on the same GPU, at both shapes, for reference;
 * ``tp_sweep``: single-rank shards at tensor-parallel degree 1, 2, 4, 8 (per-rank
   hidden width 28672 / k) and M in {1, 8, 32, 64, 4096}, each against its roofline;
 * ``all_shards_m2048``: the eight TP=8 shards and their partials sum at M = 2048;
@@ -303,6 +305,56 @@ def run_prefill(tpm, lib, synth, dev, iters, warmup):
     plan = {k: r.shard.plan[k] for k in ("packed_weight_bytes", "workspace_bytes")}
     r.shard.close()
     return (t1 - t0) / iters, k1, k2, plan
+
+
+def run_vendor_gemm(synth, dev, host_inputs, reps_decode, reps_prefill):
+    """The shard's two products on the vendor GEMM (torch.matmul, which calls hipBLASLt),
+    plain bf16 output and no epilogue, on the same GPU, for reference: at the decode
+    shape (M = 32) over the 8 ranks' weights in turn, as the decode step streams them,
+    and at the prefill shape (M = 8192) on rank 0's weights.  Each product is timed as
+    a run of back-to-back calls between two events (time per call); not part of the
+    library."""
+    import torch
+    x_cpu, a_sh, b_sh = host_inputs
+    F = FFN // TP
+    A = [a.to(dev) for a in a_sh]
+    B = [b.to(dev) for b in b_sh]
+    g = torch.Generator(device="cpu").manual_seed(4242)
+
+    def per_call(fn, calls, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(calls):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / calls
+
+    res = {"library": "torch.matmul -> hipBLASLt, bf16 in and out, fp32 accumulation, no epilogue"}
+    x = x_cpu.to(dev)
+    h = (torch.randn(M_DECODE, F, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    t1 = per_call(lambda i: x @ A[i % TP], reps_decode, 2 * TP)
+    t2 = per_call(lambda i: h @ B[i % TP], reps_decode, 2 * TP)
+    w1, w2 = D_MODEL * 2 * F * 2, F * D_MODEL * 2
+    res["decode_m32"] = {"gate_up_us": round(t1 * 1e6, 2), "down_us": round(t2 * 1e6, 2),
+                         "gate_up_GBs_weights": round(w1 / t1 / 1e9, 1),
+                         "down_GBs_weights": round(w2 / t2 / 1e9, 1)}
+    del x, h
+    xp = synth.tokens(M_PREFILL).to(dev)
+    hp = (torch.randn(M_PREFILL, F, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    t1 = per_call(lambda i: xp @ A[0], reps_prefill, reps_prefill)
+    t2 = per_call(lambda i: hp @ B[0], reps_prefill, reps_prefill)
+    f1, f2 = 2 * M_PREFILL * D_MODEL * 2 * F, 2 * M_PREFILL * F * D_MODEL
+    res["prefill_m8192"] = {"gate_up_us": round(t1 * 1e6, 1), "down_us": round(t2 * 1e6, 1),
+                            "gate_up_TFLOPs": round(f1 / t1 / 1e12, 1),
+                            "down_TFLOPs": round(f2 / t2 / 1e12, 1)}
+    del xp, hp, A, B
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 SWEEP_TP = (1, 2, 4, 8)
@@ -809,6 +861,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the tensor-parallel degree sweep and the M=2048 eight-shard step")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the same products on the vendor GEMM (torch.matmul)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
@@ -909,6 +963,19 @@ def main():
                             "avg_launch_us": round(p2_ms * 1e3, 1)}}
         log("prefill: %.3f ms/call, %.1f TFLOP/s" % (t_call * 1e3, tf))
 
+    vendor = None
+    if not args.no_vendor:
+        if ranks is not None:
+            for r in ranks:
+                r.shard.close()
+            ranks = None
+            torch.cuda.empty_cache()
+        log("vendor GEMM on the same products ...")
+        vendor = run_vendor_gemm(synth, dev, host_inputs, args.steps, args.prefill_iters)
+        log("vendor GEMM: decode gate/up %.2f us, down %.2f us; prefill gate/up %.1f us, down %.1f us"
+            % (vendor["decode_m32"]["gate_up_us"], vendor["decode_m32"]["down_us"],
+               vendor["prefill_m8192"]["gate_up_us"], vendor["prefill_m8192"]["down_us"]))
+
     sweep = all_shards = None
     if not args.no_sweep:
         if ranks is not None:
@@ -966,6 +1033,7 @@ def main():
                                  "sees it, gap between the launches included: one pass over "
                                  "the 8 ranks captured in a HIP graph, replay time / 8"},
         "prefill": prefill,
+        "vendor_gemm": vendor,
         "tp_sweep": sweep,
         "all_shards_m2048": all_shards,
         "attention_projections": attn,
