@@ -6,37 +6,34 @@
 // gfx950 compute unit when the matrix cores are meant to stay busy:
 //
 //  * Block tile 256 x 256 (tokens x columns), 8 waves (two per SIMD), each owning a
-//    128 x 64 sub-tile: 128 fp32 sums per lane.  The library multiplies with 16x16x32
-//    products (GF_M16: 32 per stage per wave, 8 row blocks x 4 column blocks), which
-//    move fewer register bytes per flop than 32x32x16 ones: flat out on every SIMD the
-//    16x16x32 loop holds a 2.14 GHz shader clock against 1.77 GHz for 32x32x16, and
-//    since the prefill products are power-limited that clock is what they gain (gate/up
-//    of the TP=8 shard at M = 8192: 785-792 -> 701-716 us).  Their fragments are
-//    gathered from the same 32x32x16 operand order with a per-lane remap (see
-//    fragA16 / fragB16).  Per stage a wave reads 8 token and 4 weight fragments (12
-//    KiB) from LDS; the second wave on the SIMD issues its products while the first
-//    waits on its reads.  The template also builds the 32x32x16 form and a 4-wave
-//    form (NW = 4: one wave per SIMD, 128 x 128 sub-tiles, a third less LDS traffic
-//    per flop), both slower here (the lone wave has nothing to issue while it waits).
+//    128 x 64 sub-tile: 128 fp32 sums per lane.  It multiplies with 16x16x32 products
+//    (32 per stage per wave, 8 row blocks x 4 column blocks), which move fewer
+//    register bytes per flop than 32x32x16 ones: flat out on every SIMD the 16x16x32
+//    loop holds a 2.14 GHz shader clock against 1.77 GHz for 32x32x16, and since the
+//    prefill products are power-limited that clock is what they gain (gate/up of the
+//    TP=8 shard at M = 8192: 785-792 us with 32x32x16 products -> 701-716 us).  Their
+//    fragments are gathered from the 32x32x16 operand order of the packed buffers with
+//    a per-lane remap (see fragA / fragB).  Per stage a wave reads 8 token and 4 weight
+//    fragments (12 KiB) from LDS; the second wave on the SIMD issues its products while
+//    the first waits on its reads.  The wave count is a template parameter: NW = 4 (one
+//    wave per SIMD, 128 x 128 sub-tiles, a third less LDS traffic per flop) measured
+//    slower, since the lone wave has nothing to issue while it waits.
 //  * Operands go from global memory straight into LDS through a ring of R stages of
 //    32 contraction indices (32 KiB each: 16 token and 16 weight chunks of 1 KiB), so
 //    R - 1 stages are in flight while one is multiplied (R = 3 in the library).  The
-//    library form (GF_BUF) uses buffer loads to LDS: one 32-bit lane offset per chunk
-//    and the stage advance in a scalar offset, where 64-bit global addresses cost two vector additions per
-//    chunk per stage.  A wave waits only for its own loads of the next stage (an
-//    exact count of its outstanding loads), then one plain barrier per stage; the
-//    loop is peeled so that the steady-state stages carry no branch around a load.
+//    loads are buffer loads to LDS: one 32-bit lane offset per chunk and the stage
+//    advance in a scalar offset (64-bit global addresses cost two vector additions per
+//    chunk per stage and measured 2-3% slower).  A wave waits only for its own loads
+//    of the next stage (an exact count of its outstanding loads), then one plain
+//    barrier per stage; the loop is peeled so that the steady-state stages carry no
+//    branch around a load.
 //  * The weight and the packed hidden buffer arrive in fragment order
-//    (tpm_internal.h): one conflict-free 1 KiB ds_read_b128 per fragment.  Row-major
-//    tokens are loaded as 64-byte row segments of 16 rows per 1 KiB chunk.  For
-//    16x16x32 products the chunk is stored transposed (piece p of row r at slot
-//    16 p + r), so that a fragment read (lane l: row l % 16, piece l / 16) is
-//    lane-contiguous: measured on MI355X, every arrangement that keeps a row's four
-//    pieces side by side costs 4 bank-conflict cycles per such read (58.5 M per
-//    gate/up launch), the transposed one none.  For 32x32x16 products the pieces stay
-//    side by side, swizzled (slot 4 (r mod 16) + (p xor sw(r)),
-//    sw(r) = ((r >> 2) + 2 ((r >> 1) & 1)) mod 4), which that read pattern takes
-//    without conflicts.
+//    (tpm_internal.h), read with conflict-free ds_read_b128.  Row-major tokens are
+//    loaded as 64-byte row segments of 16 rows per 1 KiB chunk, stored transposed
+//    (piece p of row r at slot 16 p + r), so that a fragment read (lane l: row l % 16,
+//    piece l / 16) is lane-contiguous: measured on MI355X, every arrangement that keeps
+//    a row's four pieces side by side costs 4 bank-conflict cycles per such read
+//    (58.5 M per gate/up launch), the transposed one none.
 //  * Tiles are renumbered XCD-contiguous (workgroup b runs on XCD b mod 8) and grouped
 //    four tile rows at a time, so the tiles an XCD runs together share operands in
 //    its L2.  When the last round of tiles would leave at least half of the compute
@@ -45,11 +42,9 @@
 //    of two values is order-free, so the result does not depend on arrival order)
 //    and runs the epilogue.
 //  * Fused epilogue: SiLU(gate) * up (a 32-column block holds 16 gate and the 16
-//    matching up columns: with 16x16x32 products they are two accumulator blocks and
-//    a feature's gate and up sums sit in the same lane; with 32x32x16 lane c meets
-//    lane c + 16 by a cross-lane exchange), tanh or identity, staged through LDS and
-//    written as bf16 in the packed hidden order; or the row-major partial store (fp32
-//    or bf16).
+//    matching up columns: two accumulator blocks, so a feature's gate and up sums sit
+//    in the same lane), tanh or identity, staged through LDS and written as bf16 in the
+//    packed hidden order; or the row-major partial store (fp32 or bf16).
 #include <type_traits>
 
 #include "device_common.h"
@@ -80,53 +75,30 @@ __device__ __forceinline__ void wait_stages(int n) {
   else wait_vmem<0>();
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
-// lds + 16 l (lds is wave-uniform).  Counted by the vector-memory counter.  The
-// builtin exists only for the device; the host pass sees an empty body.
-__device__ __forceinline__ void dma16(const void *g, void *lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
-#endif
-}
-
-// Swizzle of the row-major token stages (rows within a 16-row chunk).
-__host__ __device__ __forceinline__ int tok_sw(int r) { return ((r >> 2) + 2 * ((r >> 1) & 1)) & 3; }
-
 }  // namespace
 
+// A wave's 128 x (32 WNB) sub-tile: acc[i][j] for 16-row block i and 16-column block j,
+// 4 fp32 sums per lane (row 4 (lane / 16) + r, column lane % 16): 128 per lane.
 template <int NW>
 struct GemmShape {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static constexpr int WNB = 16 / NW;             // 32-column blocks per wave
-  static constexpr int PW = kStageChunks / NW;    // chunks each wave loads per stage
-  static constexpr int NF = 4 + WNB;              // fragments per k-step per wave
-};
-
-// Accumulators of a wave's 128 x (32 WNB) sub-tile, 128 fp32 per lane either way:
-// 32x32x16 products hold acc[i][j] for 32-row block i and 32-column block j (16 sums
-// per lane); 16x16x32 products hold acc[i][j] for 16-row block i and 16-column block j
-// (4 sums per lane).
-template <int NW, bool M16>
-struct GemmAcc {
-  static constexpr int WNB = 16 / NW;
-  static constexpr int AI = M16 ? 8 : 4;         // row blocks
-  static constexpr int AJ = M16 ? 2 * WNB : WNB;  // column blocks
-  static constexpr int RPA = M16 ? 4 : 16;       // sums per lane per block
-  using T = std::conditional_t<M16, f32x4_t, f32x16_t>;
+  static constexpr int WNB = 16 / NW;  // 32-column blocks per wave
+  static constexpr int AI = 8;         // 16-row blocks
+  static constexpr int AJ = 2 * WNB;   // 16-column blocks
 };
 
 // Epilogue of a 256 x 256 tile held by NW waves as 128 x (32 WNB) sub-tiles (wave at
 // row half wm, column group wn): SiLU(gate) * up, tanh or identity written as bf16 into
 // the packed hidden buffer (staged through the LDS ring, free after the main loop), or
 // the row-major partial store.
-template <int EPI, int NW, int R, bool M16, typename AccT, int AI, int AJ>
-__device__ __forceinline__ void gemm_epilogue(AccT (&acc)[AI][AJ], u32x4_t (*lds)[kStageChunks][64],
-                                              int wave, int wm, int wn, int lane, int tn, int row0,
-                                              int M, void *__restrict__ out, int64_t ldo, int n_store,
+template <int EPI, int NW, int R>
+__device__ __forceinline__ void gemm_epilogue(f32x4_t (&acc)[GemmShape<NW>::AI][GemmShape<NW>::AJ],
+                                              u32x4_t (*lds)[kStageChunks][64], int wave, int wm,
+                                              int wn, int lane, int tn, int row0, int M,
+                                              void *__restrict__ out, int64_t ldo, int n_store,
                                               int ks_out) {
-  using Ac = GemmAcc<NW, M16>;
-  static_assert(AI == Ac::AI && AJ == Ac::AJ, "accumulator layout");
-  constexpr int WNB = 16 / NW;
+  using Sh = GemmShape<NW>;
+  constexpr int WNB = Sh::WNB;
   constexpr bool HIDDEN = writes_hidden(EPI);
   if constexpr (HIDDEN) {
     // h of the wave's 128 rows, BPP column blocks (JW features each) per pass, staged
@@ -144,38 +116,20 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[AI][AJ], u32x4_t (*lds
 #pragma unroll
       for (int jj = 0; jj < BPP; ++jj) {
         const int j = pass * BPP + jj;
-        if constexpr (M16) {
-          // 32-column block j is 16-column blocks 2 j (gate, or its first half) and
-          // 2 j + 1 (up, or its second half): gate and up of a feature share a lane
+        // 32-column block j is 16-column blocks 2 j (gate, or its first half) and 2 j + 1
+        // (up, or its second half): gate and up of a feature share a lane
 #pragma unroll
-          for (int i = 0; i < Ac::AI; ++i) {
+        for (int i = 0; i < Sh::AI; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int rr = 16 * i + 4 * (lane >> 4) + r;
-              const int c = lane & 15;
-              const float v = acc[i][2 * j][r], u = acc[i][2 * j + 1][r];
-              if constexpr (EPI == EPI_SILU_GATE) {
-                hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
-              } else {
-                hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
-                hs[rr * HS + jj * 32 + 16 + c] = f32_to_bf16(act_f<EPI>(u));
-              }
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < Ac::AI; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = i * 32 + mfma32_row(r, lane);
-              const int c = lane & 31;
-              const float v = acc[i][j][r];
-              if constexpr (EPI == EPI_SILU_GATE) {
-                const float u = __shfl_xor(v, 16);
-                if (c < 16) hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
-              } else {
-                hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
-              }
+          for (int r = 0; r < 4; ++r) {
+            const int rr = 16 * i + 4 * (lane >> 4) + r;
+            const int c = lane & 15;
+            const float v = acc[i][2 * j][r], u = acc[i][2 * j + 1][r];
+            if constexpr (EPI == EPI_SILU_GATE) {
+              hs[rr * HS + jj * 16 + c] = f32_to_bf16(silu_f(v) * u);
+            } else {
+              hs[rr * HS + jj * 32 + c] = f32_to_bf16(act_f<EPI>(v));
+              hs[rr * HS + jj * 32 + 16 + c] = f32_to_bf16(act_f<EPI>(u));
             }
           }
         }
@@ -196,16 +150,14 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[AI][AJ], u32x4_t (*lds
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < Ac::AI; ++i) {
+    for (int i = 0; i < Sh::AI; ++i) {
 #pragma unroll
-      for (int r = 0; r < Ac::RPA; ++r) {
-        const int row = row0 + wm * 128 +
-                        (M16 ? 16 * i + 4 * (lane >> 4) + r : 32 * i + mfma32_row(r, lane));
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + wm * 128 + 16 * i + 4 * (lane >> 4) + r;
         if (row >= M) continue;
 #pragma unroll
-        for (int j = 0; j < Ac::AJ; ++j) {
-          const int col = M16 ? (tn * 8 + wn * WNB) * 32 + 16 * j + (lane & 15)
-                              : (tn * 8 + wn * WNB + j) * 32 + (lane & 31);
+        for (int j = 0; j < Sh::AJ; ++j) {
+          const int col = (tn * 8 + wn * WNB) * 32 + 16 * j + (lane & 15);
           const int64_t o = static_cast<int64_t>(row) * ldo + col;
           if constexpr (stores_f32(EPI)) {
             if (col < n_store) static_cast<float *>(out)[o] = acc[i][j][r];
@@ -218,14 +170,6 @@ __device__ __forceinline__ void gemm_epilogue(AccT (&acc)[AI][AJ], u32x4_t (*lds
   }
 }
 
-// Kernel flags: GF_BUF loads the operands with buffer instructions (one 32-bit lane
-// offset per chunk, the stage advance in a scalar offset) instead of 64-bit global
-// addresses; GF_AGPR keeps the accumulators in the accumulation registers; GF_M16
-// multiplies with 16x16x32 products instead of 32x32x16.
-constexpr int GF_BUF = 1;
-constexpr int GF_AGPR = 2;
-constexpr int GF_M16 = 4;
-
 // Buffer descriptor of a raw byte-addressed buffer (gfx9 layout: dword 3 = 0x00020000,
 // 32-bit data format, no swizzle); every access made through it stays in bounds by
 // construction, so the record count is the largest one.
@@ -233,6 +177,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), static_cast<short>(0),
                                            static_cast<int>(0xffffffffu), 0x00020000);
 }
+// 16 bytes per lane from global memory (buffer r, byte offset voff + soff) straight
+// into LDS: lane l's bytes land at lds + 16 l (lds is wave-uniform).  Counted by the
+// vector-memory counter.  The builtin exists only for the device; the host pass sees
+// an empty body.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff,
                                           void *lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -241,17 +189,15 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned vof
 #endif
 }
 
-template <int EPI, int NW, int R, int FL>
+template <int EPI, int NW, int R>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
        const u32x4_t *__restrict__ W, int ks_a, int ntm, int ntn, void *__restrict__ out,
        int64_t ldo, int n_store, int ks_out, int n_whole, uint64_t *__restrict__ split_buf,
        int *__restrict__ split_cnt) {
   constexpr bool FIRST = tokens_row_major(EPI);  // row-major token operand
-  constexpr bool M16 = (FL & GF_M16) != 0;       // 16x16x32 products
-  constexpr bool TT = M16;                       // transposed row-major token chunks
   using Sh = GemmShape<NW>;
-  constexpr int WNB = Sh::WNB, NF = Sh::NF;
+  constexpr int WNB = Sh::WNB, AI = Sh::AI, AJ = Sh::AJ;
   constexpr int PT = 16 / NW;   // token chunks each wave loads per stage
   constexpr int PWW = 16 / NW;  // weight chunks each wave loads per stage
   constexpr int PW = PT + PWW;
@@ -299,8 +245,8 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   // Stage layout: chunks 0..15 hold the token operand, 16..31 the weight: chunk
   // 16 + 8 ks + cb is the weight fragment of column block cb of the tile at k-step ks
   // of the stage; for the packed hidden buffer chunk 8 ks + rb is the fragment of row
-  // block rb; for row-major tokens chunk c holds tile rows 16 c .. 16 c + 15 (64
-  // bytes each, swizzled).  The direct-to-LDS load puts lane l's 16 bytes at 16 l of
+  // block rb; for row-major tokens chunk c holds 64 bytes of tile rows 16 c ..
+  // 16 c + 15, transposed (piece p of row r at slot 16 p + r).  The direct-to-LDS load puts lane l's 16 bytes at 16 l of
   // the chunk, so each source offset is the lane's own piece of that chunk.  Wave w
   // loads token chunks [PT w, PT w + PT) and weight chunks 16 + [PWW w, PWW w + PWW).
   // Offsets are in bytes from per-tile bases: the token rows of the tile and the
@@ -314,17 +260,12 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
 #pragma unroll
   for (int q = 0; q < PT; ++q) {
     const int c = PT * wave + q;
-    if constexpr (FIRST && TT) {
-      // transposed token chunk (16x16x32 form): lane l holds piece l / 16 of row
-      // l % 16, so that a fragment read is lane-contiguous
+    if constexpr (FIRST) {
+      // transposed token chunk: lane l holds piece l / 16 of row l % 16, so that a
+      // fragment read is lane-contiguous
       const int r = 16 * c + (lane & 15);
       const int rr = row0 + r < M ? r : M - 1 - row0;  // rows past the end repeat the last
       tvo[q] = static_cast<unsigned>((static_cast<int64_t>(rr) * lda + 8 * (lane >> 4)) * 2);
-    } else if constexpr (FIRST) {
-      const int r = 16 * c + (lane >> 2);
-      const int rr = row0 + r < M ? r : M - 1 - row0;  // rows past the end repeat the last
-      const int piece = (lane & 3) ^ tok_sw(r & 15);
-      tvo[q] = static_cast<unsigned>((static_cast<int64_t>(rr) * lda + 8 * piece) * 2);
     } else {
       const int ks = c >> 3, rb = c & 7;
       tvo[q] = static_cast<unsigned>(((rb * ks_a + ks) * 64 + lane) * 16);
@@ -340,69 +281,41 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   auto issue = [&](int kt, int buf, int q) {
     const unsigned st = static_cast<unsigned>(k_lo + kt);
     if (q < PT) {
-      if constexpr ((FL & GF_BUF) != 0)
-        dma16_buf(trs, tvo[q], st * tstep, &lds[buf][PT * wave + q][0]);
-      else
-        dma16(reinterpret_cast<const char *>(tbase) + tvo[q] + st * tstep, &lds[buf][PT * wave + q][0]);
+      dma16_buf(trs, tvo[q], st * tstep, &lds[buf][PT * wave + q][0]);
     } else {
       const int qq = q - PT;
-      if constexpr ((FL & GF_BUF) != 0)
-        dma16_buf(wrs, wvo[qq], st * wstep, &lds[buf][16 + PWW * wave + qq][0]);
-      else
-        dma16(reinterpret_cast<const char *>(wbase) + static_cast<uint64_t>(wvo[qq]) + static_cast<uint64_t>(st) * wstep,
-              &lds[buf][16 + PWW * wave + qq][0]);
+      dma16_buf(wrs, wvo[qq], st * wstep, &lds[buf][16 + PWW * wave + qq][0]);
     }
   };
 
-  using Ac = GemmAcc<NW, M16>;
-  typename Ac::T acc[Ac::AI][Ac::AJ];
+  f32x4_t acc[AI][AJ];
 #pragma unroll
-  for (int i = 0; i < Ac::AI; ++i)
+  for (int i = 0; i < AI; ++i)
 #pragma unroll
-    for (int j = 0; j < Ac::AJ; ++j)
+    for (int j = 0; j < AJ; ++j)
 #pragma unroll
-      for (int r = 0; r < Ac::RPA; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
   auto mma = [&](int i, int j, const u32x4_t &a, const u32x4_t &w) {
-    if constexpr (M16) acc[i][j] = mfma_16x16x32(a, w, acc[i][j]);
-    else acc[i][j] = mfma_32x32x16(a, w, acc[i][j]);
-    if constexpr ((FL & GF_AGPR) != 0) asm("" : "+a"(acc[i][j]));
+    acc[i][j] = mfma_16x16x32(a, w, acc[i][j]);
   };
 
-  // Fragment reads.  f < 4: token row block 4 wm + f; else weight column block
-  // WNB wn + f - 4.
+  // Fragments of a whole stage (its 32 contraction indices).  The packed buffers hold
+  // the 32x32x16 operand order (two k-steps of 16, lane halves of 8); the k-group
+  // g = lane / 16 of a 16x16x32 operand is k-step g & 1, lane half g >> 1 of that
+  // order, so A and B agree on the contraction order.  Each 16-lane group reads 256
+  // contiguous bytes (row-major tokens: the whole transposed chunk, lane by lane),
+  // free of bank conflicts.
   const u32x4_t *lds_flat = &lds[0][0][0];
-  const int tok_slot = 4 * (lane & 15);
-  const int tok_x = tok_sw(lane & 15);
-  auto frag = [&](int buf, int ks, int f) -> u32x4_t {
-    if (f < 4) {
-      const int rb = 4 * wm + f;
-      if constexpr (FIRST) {
-        const int chunk = 2 * rb + ((lane & 31) >> 4);
-        const int piece = 2 * (lane >> 5) + ks;
-        return lds_flat[(buf * kStageChunks + chunk) * 64 + tok_slot + (piece ^ tok_x)];
-      } else {
-        return lds[buf][8 * ks + rb][lane];
-      }
-    }
-    return lds[buf][16 + 8 * ks + WNB * wn + (f - 4)][lane];
-  };
-  // 16x16x32 fragments of a whole stage (its 32 contraction indices), gathered from
-  // the same chunks: the k-group g = lane / 16 of a 16x16x32 operand is k-step g & 1,
-  // lane half g >> 1 of the stage's 32x32x16 pair, so A and B agree on the order.
-  // Each 16-lane group reads 256 contiguous bytes (row-major tokens: the whole
-  // transposed chunk, lane by lane), free of bank conflicts.
   const int g16 = lane >> 4, r16 = lane & 15;
-  auto fragA16 = [&](int buf, int ri) -> u32x4_t {  // rows 16 ri .. 16 ri + 15 of the wave's 128
-    const int row = wm * 128 + 16 * ri + r16;        // row of the tile
-    if constexpr (FIRST && TT) {
+  auto fragA = [&](int buf, int ri) -> u32x4_t {  // rows 16 ri .. 16 ri + 15 of the wave's 128
+    const int row = wm * 128 + 16 * ri + r16;      // row of the tile
+    if constexpr (FIRST) {
       return lds_flat[(buf * kStageChunks + (row >> 4)) * 64 + lane];
-    } else if constexpr (FIRST) {
-      return lds_flat[(buf * kStageChunks + (row >> 4)) * 64 + tok_slot + (g16 ^ tok_x)];
     } else {
       return lds[buf][8 * (g16 & 1) + (row >> 5)][32 * (g16 >> 1) + (row & 31)];
     }
   };
-  auto fragB16 = [&](int buf, int cj) -> u32x4_t {  // columns 16 cj .. of the wave's 32 WNB
+  auto fragB = [&](int buf, int cj) -> u32x4_t {  // columns 16 cj .. of the wave's 32 WNB
     const int cb = WNB * wn + (cj >> 1);
     return lds[buf][16 + 8 * (g16 & 1) + cb][32 * (g16 >> 1) + 16 * (cj & 1) + r16];
   };
@@ -442,67 +355,24 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  // 32x32x16: NF fragments of a k-step; 16x16x32: 4 A and 2 WNB B fragments
-  constexpr int NFR = M16 ? 4 + 2 * WNB : NF;
-  u32x4_t f0[NFR], f1[NFR];
-  if constexpr (M16) {
-    // f0[0..3]: A row blocks 0..3, f0[4..4 + AJ): the B blocks; f1[0..3]: A 4..7
+  // f0[0..3]: A row blocks 0..3, f0[4 .. 4 + AJ): the B blocks; f1: A row blocks 4..7
+  u32x4_t f0[4 + AJ], f1[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f0[i] = fragA16(0, i);
+  for (int i = 0; i < 4; ++i) f0[i] = fragA(0, i);
 #pragma unroll
-    for (int j = 0; j < Ac::AJ; ++j) f0[4 + j] = fragB16(0, j);
-  } else {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) f0[f] = frag(0, 0, f);
-  }
+  for (int j = 0; j < AJ; ++j) f0[4 + j] = fragB(0, j);
 
-  // Stage kt: k-step 0 multiplies f0 while k-step 1's fragments are read into f1;
-  // then (sync) k-step 1 multiplies f1 while the buffer of stage kt is refilled
-  // with stage kt + R and the next stage's first fragments are read into f0.  The
-  // scheduling barriers keep one fragment read or load between products.  REFILL
-  // and MORE are compile-time so the steady-state loop has no branches: the last R
-  // stages run in a peeled tail.
-  auto stage32 = [&](int kt, int buf, auto refill_c, auto more_c) {
+  // Stage kt: the first half multiplies row blocks 0..3 (f0) by every column block
+  // while row blocks 4..7 are read into f1; then (sync) the second half multiplies row
+  // blocks 4..7, column block by column block, so that each B fragment is dead after
+  // its four products and the next stage's copy can be read in its place; meanwhile
+  // the buffer of stage kt is refilled with stage kt + R and the next stage's row
+  // blocks 0..3 are read.  The scheduling barriers keep one fragment read or load
+  // between products.  REFILL and MORE are compile-time so the steady-state loop has
+  // no branches: the last R stages run in a peeled tail.
+  auto stage = [&](int kt, int buf, auto refill_c, auto more_c) {
     constexpr bool REFILL = decltype(refill_c)::value;
     constexpr bool MORE = decltype(more_c)::value;
-    const int nbuf = buf + 1 == R ? 0 : buf + 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < WNB; ++j) {
-        mma(i, j, f0[i], f0[4 + j]);
-        __builtin_amdgcn_sched_barrier(0);
-        const int q = i * WNB + j;
-        if (q < NF) f1[q] = frag(buf, 1, q);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if constexpr (MORE) sync_mid(kt, refill_c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < WNB; ++j) {
-        mma(i, j, f1[i], f1[4 + j]);
-        __builtin_amdgcn_sched_barrier(0);
-        const int q = i * WNB + j;
-        if constexpr (REFILL)
-          if (q < PW) issue(kt + R, buf, q);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (MORE)
-          if (q < NF) f0[q] = frag(nbuf, 0, q);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-  // The same stage with 16x16x32 products: the first half multiplies row blocks 0..3
-  // (f0) by every column block while row blocks 4..7 are read into f1; then (sync) the
-  // second half multiplies row blocks 4..7, column block by column block, so that each
-  // B fragment is dead after its four products and the next stage's copy can be read
-  // in its place; the next stage's row blocks 0..3 are read meanwhile.
-  auto stage16 = [&](int kt, int buf, auto refill_c, auto more_c) {
-    constexpr bool REFILL = decltype(refill_c)::value;
-    constexpr bool MORE = decltype(more_c)::value;
-    constexpr int AJ = Ac::AJ;
     const int nbuf = buf + 1 == R ? 0 : buf + 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -510,7 +380,7 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
       for (int j = 0; j < AJ; ++j) {
         mma(i, j, f0[i], f0[4 + j]);
         __builtin_amdgcn_sched_barrier(0);
-        if (j == 0) f1[i] = fragA16(buf, 4 + i);
+        if (j == 0) f1[i] = fragA(buf, 4 + i);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -526,16 +396,12 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
           if (q < PW) issue(kt + R, buf, q);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (MORE) {
-          if (j == 0) f0[i] = fragA16(nbuf, i);
-          if (i == 3) f0[4 + j] = fragB16(nbuf, j);
+          if (j == 0) f0[i] = fragA(nbuf, i);
+          if (i == 3) f0[4 + j] = fragB(nbuf, j);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  };
-  auto stage = [&](int kt, int buf, auto refill_c, auto more_c) {
-    if constexpr (M16) stage16(kt, buf, refill_c, more_c);
-    else stage32(kt, buf, refill_c, more_c);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
@@ -556,18 +422,18 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     // point once counted), count the workgroup in; the second to arrive reads the
     // other half's sums with coherent loads and goes on.
     int *s_second = reinterpret_cast<int *>(&lds[0][0][0]);  // the ring is free now
-    constexpr int NV = Ac::AI * Ac::AJ * Ac::RPA / 2;  // 64-bit pairs of sums per thread
+    constexpr int NV = AI * AJ * 2;  // 64-bit pairs of sums per thread
     uint64_t *mine = split_buf + (static_cast<int64_t>(pair) * 2 + khalf) * (NW * 64 * NV);
     uint64_t *other = split_buf + (static_cast<int64_t>(pair) * 2 + (khalf ^ 1)) * (NW * 64 * NV);
 #pragma unroll
-    for (int i = 0; i < Ac::AI; ++i)
+    for (int i = 0; i < AI; ++i)
 #pragma unroll
-      for (int j = 0; j < Ac::AJ; ++j)
+      for (int j = 0; j < AJ; ++j)
 #pragma unroll
-        for (int r = 0; r < Ac::RPA; r += 2) {
+        for (int r = 0; r < 4; r += 2) {
           const uint64_t v = static_cast<uint64_t>(__float_as_uint(acc[i][j][r])) |
                              (static_cast<uint64_t>(__float_as_uint(acc[i][j][r + 1])) << 32);
-          __hip_atomic_store(&mine[((i * Ac::AJ + j) * (Ac::RPA / 2) + r / 2) * (NW * 64) + tid], v,
+          __hip_atomic_store(&mine[((i * AJ + j) * 2 + r / 2) * (NW * 64) + tid], v,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     // The stores above are complete at the coherence point once the wave's memory
@@ -589,41 +455,40 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
     __syncthreads();  // every wave has read the flag before the epilogue reuses the ring
     if (!second) return;
 #pragma unroll
-    for (int i = 0; i < Ac::AI; ++i)
+    for (int i = 0; i < AI; ++i)
 #pragma unroll
-      for (int j = 0; j < Ac::AJ; ++j)
+      for (int j = 0; j < AJ; ++j)
 #pragma unroll
-        for (int r = 0; r < Ac::RPA; r += 2) {
-          const uint64_t v = __hip_atomic_load(&other[((i * Ac::AJ + j) * (Ac::RPA / 2) + r / 2) * (NW * 64) + tid],
+        for (int r = 0; r < 4; r += 2) {
+          const uint64_t v = __hip_atomic_load(&other[((i * AJ + j) * 2 + r / 2) * (NW * 64) + tid],
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           acc[i][j][r] += __uint_as_float(static_cast<uint32_t>(v));
           acc[i][j][r + 1] += __uint_as_float(static_cast<uint32_t>(v >> 32));
         }
   }
-  gemm_epilogue<EPI, NW, R, M16>(acc, lds, wave, wm, wn, lane, tn, row0, M, out, ldo, n_store, ks_out);
+  gemm_epilogue<EPI, NW, R>(acc, lds, wave, wm, wn, lane, tn, row0, M, out, ldo, n_store, ks_out);
 }
 
 }  // namespace tpm
 
 namespace tpm {
 
-// The configuration the library launches: 8 waves, 16x16x32 products, a 3-stage ring,
-// buffer loads (TP=8 shard at M = 8192, medians of 20 launches; gate/up / down:
-// 32x32x16 with a 4-stage ring 785-792 / 373-374 us, 16x16x32 with 4 stages 710-716 /
-// 370 us, with 3 stages 701-704 / 367-369 us; 16x16x32 on 4 waves 752-767 / 372-382 us).
+// The configuration the library launches: 8 waves, a 3-stage ring (TP=8 shard at
+// M = 8192, medians of 20 launches; gate/up / down: 4 stages 710-716 / 370 us, 3 stages
+// 701-704 / 367-369 us, 4 waves 752-767 / 372-382 us; with 32x32x16 products and 4
+// stages, a form since removed, 785-792 / 373-374 us).
 constexpr int kGemmWaves = 8;
 constexpr int kGemmRing = 3;
-constexpr int kGemmFlags = GF_BUF | GF_M16;
 
-template <int EPI, int NW = kGemmWaves, int R = kGemmRing, int FL = kGemmFlags>
+template <int EPI, int NW = kGemmWaves, int R = kGemmRing>
 hipError_t launch_gemm_one(const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
                            int64_t n_packed, void *out, int64_t ldo, int64_t n_store,
                            int64_t ks_out, const TiledSplit &sp, hipStream_t s, const Timing &t) {
   if (K % kGemmK || n_packed % kTileN || M < 1) return hipErrorInvalidValue;
-  // Buffer offsets are 32-bit: operands of 4 GiB or more take the global-address form
+  // Buffer offsets are 32-bit: operands past that reach take the global-address form
   // of the tiled kernel instead.
   const int64_t w_bytes = K * n_packed * 2, tile_rows_bytes = kTileM * (tokens_row_major(EPI) ? lda * 2 : K * 2);
-  if ((FL & GF_BUF) && (w_bytes >= (int64_t(1) << 32) || tile_rows_bytes >= (int64_t(1) << 31)))
+  if (w_bytes >= (int64_t(1) << 32) || tile_rows_bytes >= (int64_t(1) << 31))
     return launch_tiled_gemm(EPI, A, lda, M, K, W, n_packed, out, ldo, n_store, ks_out, sp, s, t);
   const int ntm = static_cast<int>((M + kTileM - 1) / kTileM);
   const int ntn = static_cast<int>(n_packed / kTileN);
@@ -632,7 +497,7 @@ hipError_t launch_gemm_one(const void *A, int64_t lda, int64_t M, int64_t K, con
                         ? tiled_split_tiles(static_cast<int64_t>(ntm) * ntn, sp.n_cu, sp.max_tiles)
                         : 0;
   const int n_whole = ntm * ntn - split;
-  hipExtLaunchKernelGGL((k_gemm<EPI, NW, R, FL>), dim3(n_whole + 2 * split), dim3(NW * 64), 0, s,
+  hipExtLaunchKernelGGL((k_gemm<EPI, NW, R>), dim3(n_whole + 2 * split), dim3(NW * 64), 0, s,
                         t.start, t.stop, 0, static_cast<const uint16_t *>(A), lda,
                         static_cast<int>(M), k_stages, static_cast<const u32x4_t *>(W),
                         static_cast<int>(K / kFragK), ntm, ntn, out, ldo,
