@@ -246,11 +246,11 @@ k_gemm(const uint16_t *__restrict__ A, int64_t lda, int M, int k_stages,
   // 16 + 8 ks + cb is the weight fragment of column block cb of the tile at k-step ks
   // of the stage; for the packed hidden buffer chunk 8 ks + rb is the fragment of row
   // block rb; for row-major tokens chunk c holds 64 bytes of tile rows 16 c ..
-  // 16 c + 15, transposed (piece p of row r at slot 16 p + r).  The direct-to-LDS load puts lane l's 16 bytes at 16 l of
-  // the chunk, so each source offset is the lane's own piece of that chunk.  Wave w
-  // loads token chunks [PT w, PT w + PT) and weight chunks 16 + [PWW w, PWW w + PWW).
-  // Offsets are in bytes from per-tile bases: the token rows of the tile and the
-  // tile's first column block.
+  // 16 c + 15, transposed (piece p of row r at slot 16 p + r).  The direct-to-LDS
+  // load puts lane l's 16 bytes at 16 l of the chunk, so each source offset is the
+  // lane's own piece of that chunk.  Wave w loads token chunks [PT w, PT w + PT) and
+  // weight chunks 16 + [PWW w, PWW w + PWW).  Offsets are in bytes from per-tile
+  // bases: the token rows of the tile and the tile's first column block.
   const uint16_t *tbase = FIRST ? A + static_cast<int64_t>(row0) * lda
                                 : A + static_cast<int64_t>(row0 >> 5) * ks_a * 512;
   const u32x4_t *wbase = W + static_cast<int64_t>(tn) * 8 * 64;

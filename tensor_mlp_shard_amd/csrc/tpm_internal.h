@@ -220,7 +220,7 @@ hipError_t launch_tiled_gemm(int epi, const void *A, int64_t lda, int64_t M, int
                              int64_t n_store, int64_t ks_out, const TiledSplit &sp, hipStream_t s,
                              const Timing &t = Timing(), const TiledGroups &grp = TiledGroups());
 
-// Prefill-path products on the one-wave-per-SIMD GEMM (k_gemm.hip): same operand and
+// Prefill-path products on the two-waves-per-SIMD GEMM (k_gemm.hip): same operand and
 // output conventions as launch_tiled_gemm (no grouped mode); K a multiple of kGemmK.
 constexpr int kGemmK = 32;  // contraction per LDS stage
 hipError_t launch_gemm(int epi, const void *A, int64_t lda, int64_t M, int64_t K, const void *W,
