@@ -51,6 +51,19 @@ def randn(shape, seed: int, std: float = 1.0, dtype=torch.float32) -> torch.Tens
     return v.to(dtype)
 
 
+def randn_device(shape, seed: int, device, std: float = 1.0, dtype=torch.float32) -> torch.Tensor:
+    """N(0, std^2) values drawn on ``device`` by torch's generator for that device,
+    seeded with ``seed``: for inputs of gigabytes, which the CPU generator would take
+    minutes to draw.  Values differ from ``randn`` with the same seed; a test reads
+    back whatever part of them its reference needs."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    v = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if std != 1.0:
+        v.mul_(torch.tensor(std, dtype=torch.float32, device=device))
+    return v.to(dtype)
+
+
 def split_columns(a: torch.Tensor, k: int):
     """k contiguous, equal column blocks of ``a``."""
     n = a.shape[1]

@@ -114,6 +114,36 @@ def test_attention_block_partials_sum_to_unsplit():
     assert err <= TOL_BF16
 
 
+def test_tiled_weight_past_32bit_offsets():
+    """A packed weight of 4 GiB (8192 x 262144 bf16) lies past the 32-bit buffer offsets
+    of the prefill GEMM, which hands such products to the tiled kernel with 64-bit
+    addresses.  The weight is drawn on the device (2^31 values) and is not periodic in
+    any index, so an offset that wrapped would read a wrong value.  Sampled rows and
+    columns against the oracle; the packed buffer is k-step-major, so every column's
+    products read across the whole 4 GiB."""
+    K, N, M = 8192, 262144, 300
+    w = synth.randn_device((K, N), seed=4242, device=DEV, std=synth.WEIGHT_STD,
+                           dtype=torch.bfloat16)
+    x = synth.tokens(M, K)
+    rows = synth.sample_rows(M, 16)
+    cols = synth.sample_rows(N, 256, seed=11)
+    w_cols = w[:, cols].cpu()
+    say("tiled projection, packed weight 4 GiB:", K, "x", N, "M", M)
+    p = tpm.Projection(w, max_tokens=M, out_dtype=torch.float32, path="tiled")
+    del w
+    try:
+        y = p.forward(x.to(DEV))
+        torch.cuda.synchronize()
+        yc = y[rows][:, cols].cpu()
+        del y
+    finally:
+        p.close()
+        torch.cuda.empty_cache()
+    err = oracle.rel_err(yc, oracle.projection(x[rows], w_cols))
+    say("err", err)
+    assert err <= TOL_BF16
+
+
 def test_zero_tokens_and_bad_calls():
     w = torch.randn(64, 32).to(torch.bfloat16).to(DEV)
     p = tpm.Projection(w, max_tokens=8)
