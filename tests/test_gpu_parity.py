@@ -212,6 +212,22 @@ def test_prefill_shard_tp8_sampled_rows():
     assert torch.isfinite(p).all()
 
 
+def test_prefill_shard_ragged_rows_in_split_round():
+    """M = 8000 on the TP=8 shard: 896 tiles, whose last round (128 tiles, tile rows 24-31)
+    runs as contraction halves, with the last tile row holding 64 of its 256 rows.
+    Sampled rows, all rows of that partial tile row among them, against the oracle."""
+    a, b = synth.ModelSpec().shard(2, 8)
+    M = 8000
+    x = synth.tokens(M)
+    say("prefill shard M=%d (ragged last tile row in the split round)" % M)
+    p = gpu_shard(a, b, x, "silu_gate", max_tokens=M)
+    rows = sorted(set(synth.sample_rows(M, 96)) | set(range(7936, M, 9)) | {7936, 7998, 7999})
+    err = oracle.rel_err(p[rows], oracle.shard_forward(x[rows], a, b, "silu_gate"))
+    say("rows", len(rows), "err", err)
+    assert err <= TOL_BF16
+    assert torch.isfinite(p).all()
+
+
 @pytest.mark.parametrize("M,nrows", [(32, None), (2048, 256)])
 def test_all_eight_shards_plus_reduce(M, nrows):
     """All 8 rank shards computed one after another, summed by tp_partials_reduce,
