@@ -1,40 +1,29 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Error measure: max|gpu - oracle| / sqrt(mean(oracle^2)) over the compared outputs.
-Bounds: 1e-5 for fp32 inputs, 2e-2 for bf16 inputs with fp32 accumulation.
+Bounds (tests/tolerances.py): 1e-5 for fp32 inputs, 2e-2 for bf16 inputs with fp32
+accumulation, plus half an ulp of a bf16 output.
 Large token counts compare a seeded subset of rows (rows are independent), always
 including the first and the last row.
 """
 import functools
 
-import numpy as np
 import pytest
 import torch
 
 import oracle
 import tensor_mlp_shard_amd as tpm
 from tensor_mlp_shard_amd import synth
+from tolerances import TOL_BF16, TOL_F32, tol_for
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-TOL_F32 = 1e-5
-TOL_BF16 = 2e-2
 DEV = "cuda"
 
 
 def say(*a):
     print(*a, flush=True)
-
-
-def tol_for(out_dtype, ref):
-    """Bound for bf16 inputs: TOL_BF16 for an fp32 output; a bf16 output adds its own
-    rounding, at most half an ulp (2^-8 of the value) per element, i.e. 2^-8 max|ref| in
-    the RMS-normalised measure."""
-    if out_dtype != torch.bfloat16:
-        return TOL_BF16
-    r = np.asarray(ref, dtype=np.float64)
-    return TOL_BF16 + 2.0 ** -8 * float(np.abs(r).max() / np.sqrt(np.mean(r * r)))
 
 
 def gpu_shard(a, b, x, act, path="auto", out_dtype=torch.float32, max_tokens=None):

@@ -2,7 +2,7 @@
 oracle, through the C ABI: the attention block's column-parallel QKV shard and
 row-parallel output shard at the 70B-class TP=8 shapes, both kernel paths, ragged
 and edge sizes, and the rank partials of the output projection summing to the
-unsplit block.  Bounds as for the MLP: 1e-5 (fp32 inputs), 2e-2 (bf16 inputs)."""
+unsplit block.  Bounds as for the MLP (tests/tolerances.py)."""
 import ctypes
 
 import pytest
@@ -11,12 +11,11 @@ import torch
 import oracle
 import tensor_mlp_shard_amd as tpm
 from tensor_mlp_shard_amd import synth
+from tolerances import TOL_BF16, TOL_F32, tol_for
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-TOL_F32 = 1e-5
-TOL_BF16 = 2e-2
 DEV = "cuda"
 
 
@@ -42,7 +41,8 @@ def test_qkv_shard_tp8(path, M):
     x = synth.tokens(M)
     say("qkv shard", path, "M", M)
     y = run_proj(wqkv, x, torch.bfloat16, path)
-    assert oracle.rel_err(y, oracle.projection(x, wqkv)) <= TOL_BF16
+    ref = oracle.projection(x, wqkv)
+    assert oracle.rel_err(y, ref) <= tol_for(torch.bfloat16, ref)
 
 
 @pytest.mark.parametrize("M", [1, 32, 2048])
