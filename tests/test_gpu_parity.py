@@ -14,7 +14,7 @@ import torch
 import oracle
 import tensor_mlp_shard_amd as tpm
 from tensor_mlp_shard_amd import synth
-from tolerances import TOL_BF16, TOL_F32, tol_for
+from tolerances import TOL_BF16, TOL_F32, tol_for, tol_hidden_rounding
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -88,6 +88,29 @@ def test_bf16_small_both_paths(path, act, M):
     err = oracle.rel_err(p, oracle.shard_forward(x, a, b, act))
     say("err", err)
     assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("path", ["stream", "tiled"])
+@pytest.mark.parametrize("act", ["silu_gate", "tanh", "identity"])
+@pytest.mark.parametrize("M,F", [(1, 1), (3, 2), (65, 1)])
+def test_bf16_smallest_shards(path, act, M, F):
+    """The smallest bf16 shards: d = 64 (one contraction stage of the first product)
+    and one or two hidden features, padded internally to a whole tile.  With so few
+    hidden features the partial is (nearly) rank one and the one bf16 rounding of H does
+    not average out, so the bound adds its worst case (tolerances.tol_hidden_rounding)."""
+    g = torch.Generator().manual_seed(100 * M + F)
+    cols = 2 * F if act == "silu_gate" else F
+    a = (torch.randn(64, cols, generator=g) * 0.2).to(torch.bfloat16)
+    b = (torch.randn(F, 64, generator=g) * 0.2).to(torch.bfloat16)
+    x = torch.randn(M, 64, generator=g).to(torch.bfloat16)
+    say("bf16 smallest", path, act, "M", M, "F", F)
+    p = gpu_shard(a, b, x, act, path=path)
+    ref = oracle.shard_forward(x, a, b, act)
+    h = oracle.shard_forward(x, a, torch.eye(F, dtype=torch.float64), act)  # H itself
+    tol = tol_hidden_rounding(h, b, ref)
+    err = oracle.rel_err(p, ref)
+    say("err", err, "bound", tol)
+    assert err <= tol
 
 
 @pytest.mark.parametrize("path", ["stream", "tiled"])
