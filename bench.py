@@ -35,7 +35,8 @@ The JSON line also carries
 * ``attn_partials_merge``: the decode-context-parallel merge of 8 ranks' attention
   partials (32 tokens x 64 heads, head width 128) on one GPU;
 * ``cpu_baseline``: the fp64 oracle on the host cores over a bounded sample of the
-  same decode workload.
+  same decode workload, and on a seeded subset of the prefill shard's token rows,
+  scaled by M / rows and labelled extrapolated.
 
 Inputs are seeded synthetic tensors (torch CPU generator), copied to the GPU
 before the timed region.  Usage: ``python bench.py [--steps K] [--warmup W]``.
