@@ -9,7 +9,9 @@
 //    contraction, so no partial sums leave the workgroup: no split-K scratch, no
 //    atomics, no cross-workgroup fences, bitwise reproducible results.  A shard
 //    of width 3584 gives 224 workgroups for the gate/up product (16 SiLU-gate
-//    features per block) and 256 for the down product, one per compute unit.
+//    features per block), about one per compute unit.  Shards too narrow to occupy
+//    the compute units slice the contraction instead, and the last arriving slice
+//    adds them in slice order (stream_plan; the hand-off is described at the kernel).
 //  * Its waves split the contraction into contiguous runs of k-steps.  Each wave
 //    streams its run of the column block with 1 KiB fully coalesced,
 //    non-temporal loads that are fed straight to the matrix cores (the weight is
@@ -18,10 +20,10 @@
 //    past the end of the run are clamped to the last k-step (an L2 hit) and the
 //    matching products are multiplied by zero, so the loop has no branch around a
 //    load and the compiler waits for exactly one batch at a time.
-//  * The token operand is small and read from L2: row-major X (the two lane
-//    halves read 64 contiguous bytes of a row per k-step pair, see the fragment
-//    order in tpm_internal.h) for the first product, the packed hidden buffer
-//    (1 KiB contiguous per wave load) for the second.
+//  * The token operand is small and read from L2: row-major X for the first product,
+//    staged per wave through LDS as whole 128-byte row segments (8 rows per wave
+//    load) and read back as fragments; the packed hidden buffer (1 KiB contiguous
+//    per wave load, straight into fragments) for the second.
 //  * A few tokens (at most 16): only the 8 or 16 token rows that exist are loaded
 //    per batch instead of the tile's 32, and fragment lanes of rows past M read
 //    row M - 1 (products never stored); for the packed hidden operand those lanes
